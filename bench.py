@@ -1,0 +1,281 @@
+"""Benchmark of the hot path on one MI355X: multi-destination all-gather + fused GEMM + all-gather.
+
+One step = one complete logical all-gather job on one GPU:
+  * all-gather: every one of the W=8 logical ranks calls ag_all_gather on its
+    1024 x 4096 fp16 input (tile 8x256, 256 programs), so every heap region
+    ends up with the 8192 x 4096 gathered tensor;
+  * fused: every one of the 8 logical ranks calls ag_gemm_all_gather with
+    A_g 1024 x 8192 and the shared B 8192 x 3584 (fp16, fp32 accumulate), so
+    every region ends up with the 8192 x 3584 gathered C.
+Inputs are seeded synthetic tensors already resident in HBM.
+
+Printed: one JSON line.  value = all-gather HBM GB/s over the whole job
+((1+W)*M_local*N*e bytes per call, W calls per step); the fused path's
+TFLOP/s is reported in the "fused" object, each with its roofline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "all-gather achieved HBM GB/s (+% peak); fused GEMM+AG TFLOP/s (+% MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+# all-gather workload: W=8 logical ranks, 1024 x 4096 fp16 per rank
+AG_W, AG_M, AG_N, AG_DTYPE, AG_TILE, AG_PROGRAMS = 8, 1024, 4096, "f16", (8, 256), 256
+# fused workload: W=8, M_local 1024, K 8192, N 3584, fp16
+FU_W, FU_M, FU_N, FU_K, FU_DTYPE = 8, 1024, 3584, 8192, "f16"
+
+
+def _src_hash(name: str) -> str:
+    with open(os.path.join(ROOT, "gemm_all_gather_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(summary: str, source: str, per_launch_alg: float):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None.
+
+    The summary records the source hash of the kernel file it was taken on;
+    a changed kernel makes the recorded counters stale (None).
+    """
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != _src_hash(source):
+        return None
+    return float(m_bytes.group(1))
+
+
+def _cpu_baseline_copy(seconds: float):
+    """The oracle's all-gather of the same workload on the host cores (a bounded sample)."""
+    import numpy as np
+    from gemm_all_gather_amd import inputs as gen
+    import oracle
+
+    e = 2
+    blk = AG_M * AG_N * e
+    S = AG_W * blk
+    ins = [gen.uniform_pm1((AG_M, AG_N), AG_DTYPE, 1, j) for j in range(AG_W)]
+    slab = np.zeros(AG_W * S, dtype=np.uint8)
+    oracle.all_gather_oracle(slab, S, ins, 0, 1, 0)        # warm-up
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.all_gather_oracle(slab, S, ins, 0, 1, 0)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    job_bytes = AG_W * (1 + AG_W) * blk
+    return {"value": job_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} whole all-gather jobs (W=8, {AG_M}x{AG_N} fp16 per rank, full 8-region heap "
+                      f"copy included) in {reps * dt:.1f} s with numpy on 1 host thread"}
+
+
+def _cpu_baseline_fused(seconds: float):
+    """The oracle's fused GEMM + all-gather for a bounded sample of output rows of one rank's call."""
+    import numpy as np
+    from gemm_all_gather_amd import inputs as gen
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    rows = 64
+    a = gen.normal_scaled((rows, FU_K), FU_DTYPE, FU_K ** -0.5, 2, 0)
+    b = gen.normal_scaled((FU_N, FU_K), FU_DTYPE, FU_K ** -0.5, 3)
+    oracle.gemm_oracle(a[:8], b, FU_DTYPE, "nk")             # warm-up
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemm_oracle(a, b, FU_DTYPE, "nk")
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    flops = 2.0 * rows * FU_N * FU_K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} x {rows} output rows of one rank's {FU_M}x{FU_N}x{FU_K} fp16 product "
+                      f"(float64 numpy matmul + rounding), {reps * dt:.1f} s; BLAS may use up to {threads} threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the W logical ranks are regions of one GPU's HBM; "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from gemm_all_gather_amd import binding as ag
+    from gemm_all_gather_amd import inputs as gen
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ag.lib()
+    dev_props = torch.cuda.get_device_properties(0)
+    stream = torch.cuda.current_stream()
+
+    # ---------------- all-gather setup
+    e = 2
+    blk = AG_M * AG_N * e
+    S_ag = AG_W * blk
+    # fused output block lives after the all-gather output in the same heap
+    fblk = FU_M * FU_N * 2
+    S = ((S_ag + FU_W * fblk) // (2 << 20) + 1) * (2 << 20)
+    slab = torch.empty(AG_W * S, dtype=torch.uint8, device="cuda")
+    slab.zero_()
+    heap = ag.Heap.wrap(slab, AG_W, S)
+    views = [heap.view(r) for r in range(AG_W)]
+    ins = [torch.from_numpy(gen.uniform_pm1((AG_M, AG_N), AG_DTYPE, 1, j).view(np.uint8).reshape(-1).copy()).cuda()
+           for j in range(AG_W)]
+    geom = views[0].geometry()
+    ag_plan = ag.plan_all_gather(geom, AG_W, 0, 1, ins[0], 0, AG_M, AG_N, AG_DTYPE, *AG_TILE, AG_PROGRAMS)
+
+    def copy_job():
+        for j in range(AG_W):
+            ag.all_gather(views[j], AG_W, 0, 1, ins[j], 0, AG_M, AG_N, AG_DTYPE, AG_TILE[0], AG_TILE[1],
+                          AG_PROGRAMS, stream)
+
+    # ---------------- fused setup
+    fused_ok = True
+    fa = [torch.from_numpy(gen.normal_scaled((FU_M, FU_K), FU_DTYPE, FU_K ** -0.5, 2, j).view(np.uint8)
+                           .reshape(-1).copy()).cuda() for j in range(FU_W)]
+    fb = torch.from_numpy(gen.normal_scaled((FU_N, FU_K), FU_DTYPE, FU_K ** -0.5, 3).view(np.uint8)
+                          .reshape(-1).copy()).cuda()
+    fu_off = S_ag
+
+    def fused_job():
+        for j in range(FU_W):
+            ag.gemm_all_gather(views[j], FU_W, 0, 1, fa[j], FU_K, fb, FU_K, fu_off, FU_M, FU_N, FU_K, FU_DTYPE,
+                               0, 0, 0, 0, stream)
+
+    try:
+        fu_plan = ag.plan_gemm_all_gather(geom, FU_W, 0, 1, fa[0], FU_K, fb, FU_K, fu_off, FU_M, FU_N, FU_K,
+                                          FU_DTYPE)
+        fused_job()
+        torch.cuda.synchronize()
+    except ag.AgError as exc:
+        if exc.status != ag.AG_ERR_UNSUPPORTED:
+            raise
+        fused_ok = False
+        fused_reason = str(exc)
+
+    # ---------------- warm-up and timed region
+    for _ in range(args.warmup):
+        copy_job()
+        if fused_ok:
+            fused_job()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        copy_job()
+        ev[k][1].record(stream)
+        if fused_ok:
+            fused_job()
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    copy_ms = sum(ev[k][0].elapsed_time(ev[k][1]) for k in range(args.steps)) / args.steps
+    fused_ms = sum(ev[k][1].elapsed_time(ev[k][2]) for k in range(args.steps)) / args.steps
+    step_ms = sum(ev[k][0].elapsed_time(ev[k][2]) for k in range(args.steps)) / args.steps
+
+    # ---------------- rates and rooflines
+    per_call_bytes = ag_plan.bytes_read + ag_plan.bytes_written          # (1+W) * M_local * N * e
+    copy_launch_s = copy_ms / 1e3 / AG_W
+    copy_gbs = AG_W * per_call_bytes / (copy_ms / 1e3) / 1e9
+    traffic = _traffic("ag_copy_kernel_w8_1024x4096_f16_pmc.md", "ag_copy.hip", per_call_bytes)
+    out = {
+        "metric": METRIC,
+        "value": round(copy_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"all-gather W={AG_W} logical ranks, {AG_M}x{AG_N} fp16 per rank, tile "
+                        f"{AG_TILE[0]}x{AG_TILE[1]}, {AG_PROGRAMS} programs (8 calls per step)"
+                        + (f" + fused GEMM+all-gather W={FU_W}, M_local={FU_M} K={FU_K} N={FU_N} fp16 "
+                           f"(8 calls per step)" if fused_ok else ""),
+            "parallelism": "one GPU; W logical ranks are heap regions",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(per_call_bytes / copy_launch_s / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(per_call_bytes / copy_launch_s / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "ag_copy_kernel<16,8,1>",
+            "alg_bytes_per_launch": per_call_bytes,
+            "avg_launch_us": round(copy_launch_s * 1e6, 3),
+        },
+        "device": {"name": dev_props.name, "cus": dev_props.multi_processor_count},
+        "plan_all_gather": {k: ag_plan.as_dict()[k] for k in ("vec_bytes", "n_programs", "threads", "total_tiles",
+                                                              "vectors_per_thread")},
+        "wall_s_timed": round(wall, 4),
+    }
+    if fused_ok:
+        flops = fu_plan.flops
+        fu_launch_s = fused_ms / 1e3 / FU_W
+        fu_tflops = FU_W * flops / (fused_ms / 1e3) / 1e12
+        out["fused"] = {
+            "metric": "fused GEMM+all-gather TFLOP/s",
+            "value": round(fu_tflops, 2),
+            "unit": "TFLOP/s",
+            "ms_per_job": round(fused_ms, 5),
+            "roofline": {
+                "bound": "mfma",
+                "achieved": round(flops / fu_launch_s / 1e12, 2),
+                "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(flops / fu_launch_s / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                "traffic": _traffic("ag_gemm_kernel_w8_1024x3584x8192_f16_pmc.md", "ag_gemm.hip", 0.0),
+                "alg_flops_per_launch": flops,
+                "avg_launch_us": round(fu_launch_s * 1e6, 3),
+            },
+            "plan": {k: fu_plan.as_dict()[k] for k in ("tile_m", "tile_n", "tile_k", "n_programs", "threads",
+                                                       "total_tiles")},
+        }
+    else:
+        out["fused"] = {"value": None, "reason": fused_reason}
+    out["copy_ms_per_job"] = round(copy_ms, 5)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline_copy(args.cpu_seconds)
+        if fused_ok:
+            out["fused"]["cpu_baseline"] = _cpu_baseline_fused(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    for v in views:
+        v.destroy()
+    heap.destroy()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

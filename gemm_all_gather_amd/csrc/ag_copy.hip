@@ -1,0 +1,254 @@
+// Persistent tiled multi-destination all-gather store loop for gfx950.
+//
+// Method (ROCm/iris #626, "Summary" and "Triton CCL all-gather"; ROCm/iris
+// #591, "Hoist the peer heap bases"):
+//   * before the tile loop, load the local heap base and every destination's
+//     heap base from the device table heap_bases once, and keep each
+//     destination as a 64-bit pointer delta (dest_base - local_base) in
+//     scalar registers;
+//   * walk the tiles of the M_local x N input with a grid stride;
+//   * load each input tile once and store it to every destination: the
+//     local region first, then the peers in rotated group order
+//     (g+1, g+2, ... mod W), with a statically unrolled destination loop.
+//
+// gfx950 specifics:
+//   * one 256-thread slice owns one tile at a time; a workgroup has U slices
+//     (blockDim.x = 256*U) so a CU keeps U tiles' loads and W*U tiles' stores
+//     in flight;
+//   * 16-byte vector accesses when N*e, the input and the output block are
+//     16-byte aligned (8/4/2 otherwise);
+//   * the per-lane byte offsets inside a tile do not depend on the tile, so
+//     they are computed once; each tile only adds a uniform (scalar) base,
+//     which lets the compiler use global_load/global_store with an SGPR base
+//     and a 32-bit VGPR offset;
+//   * the next tile's loads are issued before the current tile's stores, so
+//     waiting for them never waits for the stores (the memory counter is in
+//     issue order), and no destination store is preceded by a full drain.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ag_internal.h"
+
+namespace ag {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Cache-policy bits of the destination stores (0 = default policy).
+#ifndef AG_COPY_STORE_AUX
+#define AG_COPY_STORE_AUX 0
+#endif
+
+// Word 3 of a raw (stride 0) buffer descriptor on gfx9-family parts:
+// 32-bit data format, no swizzle, bounds-checked by num_records.
+constexpr int kRawBufferWord3 = 0x00020000;
+// A lane offset that is always past num_records (<= 0x7fffffff): the access
+// is dropped by the hardware (store) or returns zero (load).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(uint64_t base, uint32_t num_records)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(num_records), kRawBufferWord3);
+}
+
+template <int VEC> struct Vec;
+template <> struct Vec<16> {
+    using T = u32x4;
+    static __device__ T load(__amdgpu_buffer_rsrc_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0); }
+    static __device__ void store(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) { __builtin_amdgcn_raw_buffer_store_b128(v, r, o, 0, AG_COPY_STORE_AUX); }
+};
+template <> struct Vec<8> {
+    using T = u32x2;
+    static __device__ T load(__amdgpu_buffer_rsrc_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0); }
+    static __device__ void store(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) { __builtin_amdgcn_raw_buffer_store_b64(v, r, o, 0, AG_COPY_STORE_AUX); }
+};
+template <> struct Vec<4> {
+    using T = unsigned int;
+    static __device__ T load(__amdgpu_buffer_rsrc_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0); }
+    static __device__ void store(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) { __builtin_amdgcn_raw_buffer_store_b32(v, r, o, 0, AG_COPY_STORE_AUX); }
+};
+template <> struct Vec<2> {
+    using T = unsigned short;
+    static __device__ T load(__amdgpu_buffer_rsrc_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b16(r, o, 0, 0); }
+    static __device__ void store(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) { __builtin_amdgcn_raw_buffer_store_b16(v, r, o, 0, AG_COPY_STORE_AUX); }
+};
+
+struct TileRef {
+    uint64_t off;        // byte offset of the tile's first element in the rank's block
+    uint32_t records;    // bytes addressable from off (0: no tile, every access dropped)
+    bool full;           // every column of the tile lies inside the row
+    uint32_t col0;       // byte column of the tile's first element
+};
+
+template <int VEC, int W, int VPT>
+__global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
+{
+    using VT = Vec<VEC>;
+    using V = typename VT::T;
+
+    // ---- prologue: translate every destination once, before the tile loop.
+    // All W table entries are requested before any is used, so the scalar
+    // loads overlap and the prologue pays one memory latency.
+    uint64_t base[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+        int gi = a.group_rank + i;
+        if (gi >= W) gi -= W;
+        base[i] = __builtin_nontemporal_load(a.heap_bases + (a.rank_start + gi * a.rank_stride));
+    }
+    const uint64_t local_base = base[0];   // i = 0 is the calling rank itself
+    const uint64_t out_local = local_base + a.rank_block_offset;
+    uint64_t dest[W];   // out_local + (dest_base - local_base): local region first, then rotated peers
+#pragma unroll
+    for (int i = 0; i < W; ++i) dest[i] = out_local + static_cast<uint64_t>(static_cast<int64_t>(base[i] - local_base));
+    const uint64_t input = reinterpret_cast<uint64_t>(a.input);
+    const uint64_t block_bytes = static_cast<uint64_t>(a.rows) * a.row_bytes;
+
+    // ---- tile-invariant lane geometry
+    const uint32_t lane = threadIdx.x & 255u;
+    // a wave never straddles two slices, so the slice index is wave-uniform
+    const uint32_t slice = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
+    const uint32_t vpr_mask = (1u << a.vecs_per_row_log2) - 1u;
+    uint32_t lane_off[VPT];   // byte offset of this lane's vector j inside a tile
+    uint32_t lane_col[VPT];   // byte column of vector j inside the tile
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const uint32_t idx = lane + 256u * j;
+        lane_col[j] = (idx & vpr_mask) * VEC;
+        lane_off[j] = (idx >> a.vecs_per_row_log2) * static_cast<uint32_t>(a.row_bytes) + lane_col[j];
+    }
+
+    const uint32_t stride = gridDim.x * a.slices;
+    uint32_t t = blockIdx.x * a.slices + slice;
+    if (t >= a.total_tiles) return;
+
+    // Tile -> (tm, tn), row-major over tiles.  Rows past M_local fall past the
+    // end of the block and are dropped by the descriptor's bounds check;
+    // columns past N are redirected out of range explicitly.
+    auto origin = [&](uint32_t tile, bool valid) {
+        TileRef r;
+        const uint32_t tm = tile / a.tiles_n;
+        const uint32_t tn = tile - tm * a.tiles_n;
+        r.col0 = tn * a.tile_row_bytes;
+        r.off = static_cast<uint64_t>(tm) * a.tile_m * a.row_bytes + r.col0;
+        const uint64_t left = valid ? block_bytes - r.off : 0;
+        r.records = static_cast<uint32_t>(left < 0x7fffffffull ? left : 0x7fffffffull);
+        r.full = r.col0 + a.tile_row_bytes <= a.row_bytes;
+        return r;
+    };
+    auto offsets = [&](const TileRef& r, uint32_t (&vo)[VPT]) {
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+            vo[j] = (r.full || r.col0 + lane_col[j] < a.row_bytes) ? lane_off[j] : kOutOfRange;
+    };
+    auto load_tile = [&](const TileRef& r, const uint32_t (&vo)[VPT], V (&v)[VPT]) {
+        const __amdgpu_buffer_rsrc_t src = make_rsrc(input + r.off, r.records);
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) v[j] = VT::load(src, vo[j]);
+    };
+    auto store_tile = [&](const TileRef& r, const uint32_t (&vo)[VPT], const V (&v)[VPT]) {
+#pragma unroll
+        for (int i = 0; i < W; ++i) {   // local region first, then the rotated peers
+            const __amdgpu_buffer_rsrc_t dst = make_rsrc(dest[i] + r.off, r.records);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) VT::store(v[j], dst, vo[j]);
+        }
+    };
+
+    // Two register sets used in turn: the next tile is loaded into one while
+    // the other is stored, with no register copy (which would wait on the
+    // prefetched loads).  Loads and stores are unconditional buffer accesses;
+    // the first step is peeled so that the loop is always entered with the
+    // same accesses in flight (one tile load issued before W*VPT stores) and
+    // each wait covers only the prefetched loads, never the stores.
+    TileRef ta = origin(t, true), tb;
+    uint32_t oa[VPT], ob[VPT];
+    V va[VPT], vb[VPT];
+    offsets(ta, oa);
+    load_tile(ta, oa, va);
+
+    uint32_t tn = t + stride;
+    bool more = tn < a.total_tiles && tn > t;   // tn > t: no wrap-around
+    tb = origin(more ? tn : t, more);
+    offsets(tb, ob);
+    load_tile(tb, ob, vb);                      // prefetch (dropped when !more)
+    store_tile(ta, oa, va);
+    if (!more) return;
+    t = tn;
+    for (;;) {
+        tn = t + stride;
+        more = tn < a.total_tiles && tn > t;
+        ta = origin(more ? tn : t, more);
+        offsets(ta, oa);
+        load_tile(ta, oa, va);
+        store_tile(tb, ob, vb);
+        if (!more) break;
+        t = tn;
+
+        tn = t + stride;
+        more = tn < a.total_tiles && tn > t;
+        tb = origin(more ? tn : t, more);
+        offsets(tb, ob);
+        load_tile(tb, ob, vb);
+        store_tile(ta, oa, va);
+        if (!more) break;
+        t = tn;
+    }
+}
+
+using CopyFn = void (*)(CopyKernelArgs);
+
+template <int VEC, int W>
+CopyFn pick_vpt(int vpt)
+{
+    switch (vpt) {
+    case 1: return ag_copy_kernel<VEC, W, 1>;
+    case 2: return ag_copy_kernel<VEC, W, 2>;
+    case 4: return ag_copy_kernel<VEC, W, 4>;
+    case 8: return ag_copy_kernel<VEC, W, 8>;
+    default: return nullptr;
+    }
+}
+
+template <int VEC>
+CopyFn pick_world(int w, int vpt)
+{
+    switch (w) {
+    case 1: return pick_vpt<VEC, 1>(vpt);
+    case 2: return pick_vpt<VEC, 2>(vpt);
+    case 3: return pick_vpt<VEC, 3>(vpt);
+    case 4: return pick_vpt<VEC, 4>(vpt);
+    case 5: return pick_vpt<VEC, 5>(vpt);
+    case 6: return pick_vpt<VEC, 6>(vpt);
+    case 7: return pick_vpt<VEC, 7>(vpt);
+    case 8: return pick_vpt<VEC, 8>(vpt);
+    default: return nullptr;
+    }
+}
+
+CopyFn pick_kernel(int vec, int w, int vpt)
+{
+    switch (vec) {
+    case 16: return pick_world<16>(w, vpt);
+    case 8: return pick_world<8>(w, vpt);
+    case 4: return pick_world<4>(w, vpt);
+    case 2: return pick_world<2>(w, vpt);
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_copy(const CopyLaunch& l, hipStream_t stream)
+{
+    CopyFn fn = pick_kernel(l.vec_bytes, l.world, l.vpt);
+    if (fn == nullptr || l.args.slices < 1 || l.args.slices > 4 || l.grid < 1)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3(l.grid), dim3(256 * l.args.slices), 0, stream, l.args);
+    return hipGetLastError();
+}
+
+}  // namespace ag

@@ -1,0 +1,573 @@
+// Host runtime of libag: symmetric heap, argument validation, launch
+// planning and the C ABI declared in include/ag.h.
+//
+// The heap follows the symmetric-heap model of iris (ROCm/iris #626,
+// "Summary"; ROCm/iris #591, "Hoist the peer heap bases"): every rank owns
+// a heap, tensors sit at the same offset in every heap, and kernels find a
+// peer's copy through a device array heap_bases.  Here the rank heaps are
+// regions of one device allocation (ROCm/iris #594, "Local validation":
+// logical ranks as separate memory on one GPU).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "ag.h"
+#include "ag_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ag_status_t ok()
+{
+    g_last_error.clear();
+    return AG_OK;
+}
+
+ag_status_t fail(ag_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ag_status_t fail(ag_status_t s, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+ag_status_t fail_hip(hipError_t e, const char* what)
+{
+    const ag_status_t s = (e == hipErrorOutOfMemory) ? AG_ERR_OUT_OF_MEMORY : AG_ERR_HIP;
+    return fail(s, "%s failed: %s (%d)", what, hipGetErrorString(e), static_cast<int>(e));
+}
+
+bool is_pow2(uint64_t v) { return v != 0 && (v & (v - 1)) == 0; }
+int log2_exact(uint64_t v)
+{
+    int l = 0;
+    while ((uint64_t{1} << l) < v) ++l;
+    return l;
+}
+uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+int elem_bytes(ag_dtype_t d)
+{
+    switch (d) {
+    case AG_F16: return 2;
+    case AG_BF16: return 2;
+    case AG_F32: return 4;
+    default: return 0;
+    }
+}
+
+// Half-open byte ranges [a0, a0+an) and [b0, b0+bn) intersect.
+bool overlaps(uint64_t a0, uint64_t an, uint64_t b0, uint64_t bn)
+{
+    return an != 0 && bn != 0 && a0 < b0 + bn && b0 < a0 + an;
+}
+
+struct HeapCore {
+    void* slab = nullptr;
+    uint64_t* table = nullptr;  // device uint64_t[n_ranks]
+    int n_ranks = 0;
+    uint64_t bytes_per_rank = 0;
+    bool owns_slab = false;
+    int device = 0;
+    int num_cus = 0;
+    std::mutex mu;
+    uint64_t bump = 0;
+
+    ~HeapCore()
+    {
+        if (table) (void)hipFree(table);
+        if (owns_slab && slab) (void)hipFree(slab);
+    }
+};
+
+}  // namespace
+
+struct ag_heap {
+    std::shared_ptr<HeapCore> core;
+    int rank = -1;
+};
+
+namespace {
+
+// Common part of create and wrap: record the device, build and upload the table.
+ag_status_t finish_heap(std::shared_ptr<HeapCore> core, ag_heap_t** out)
+{
+    hipError_t e = hipGetDevice(&core->device);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    e = hipDeviceGetAttribute(&core->num_cus, hipDeviceAttributeMultiprocessorCount, core->device);
+    if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(multiProcessorCount)");
+    std::vector<uint64_t> bases(core->n_ranks);
+    for (int r = 0; r < core->n_ranks; ++r)
+        bases[r] = reinterpret_cast<uint64_t>(core->slab) + static_cast<uint64_t>(r) * core->bytes_per_rank;
+    e = hipMalloc(reinterpret_cast<void**>(&core->table), sizeof(uint64_t) * core->n_ranks);
+    if (e != hipSuccess) {
+        core->table = nullptr;
+        return fail_hip(e, "hipMalloc(heap_bases)");
+    }
+    e = hipMemcpy(core->table, bases.data(), sizeof(uint64_t) * core->n_ranks, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpy(heap_bases)");
+    auto* h = new (std::nothrow) ag_heap;
+    if (!h) return fail(AG_ERR_OUT_OF_MEMORY, "host allocation of the heap handle failed");
+    h->core = std::move(core);
+    h->rank = -1;
+    *out = h;
+    return ok();
+}
+
+ag_status_t check_geometry(const ag_heap_geometry_t* g)
+{
+    if (!g) return fail(AG_ERR_INVALID_ARG, "geometry is NULL");
+    if (g->n_ranks < 1) return fail(AG_ERR_INVALID_ARG, "n_ranks %d < 1", g->n_ranks);
+    if (g->bytes_per_rank == 0 || g->bytes_per_rank % 256 != 0)
+        return fail(AG_ERR_INVALID_ARG, "bytes_per_rank %llu is not a positive multiple of 256",
+                    static_cast<unsigned long long>(g->bytes_per_rank));
+    if (g->slab_addr == 0 || g->slab_addr % 256 != 0)
+        return fail(AG_ERR_INVALID_ARG, "slab address is null or not 256-byte aligned");
+    if (g->num_cus < 1) return fail(AG_ERR_INVALID_ARG, "num_cus %d < 1", g->num_cus);
+    if (g->rank < 0 || g->rank >= g->n_ranks)
+        return fail(AG_ERR_INVALID_ARG, "the heap handle is not a view of a rank (rank %d, n_ranks %d); use ag_heap_view",
+                    g->rank, g->n_ranks);
+    return AG_OK;
+}
+
+// Group checks shared by both operations; sets *g_out to the group rank.
+ag_status_t check_group(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride, int* g_out)
+{
+    if (W < 1) return fail(AG_ERR_INVALID_ARG, "W %d < 1", W);
+    if (W > AG_MAX_WORLD) return fail(AG_ERR_UNSUPPORTED, "W %d > %d", W, AG_MAX_WORLD);
+    if (rank_start < 0) return fail(AG_ERR_INVALID_ARG, "rank_start %d < 0", rank_start);
+    if (rank_stride < 1) return fail(AG_ERR_INVALID_ARG, "rank_stride %d < 1", rank_stride);
+    const int64_t last = static_cast<int64_t>(rank_start) + static_cast<int64_t>(W - 1) * rank_stride;
+    if (last >= geom->n_ranks)
+        return fail(AG_ERR_INVALID_ARG, "group member %lld is past the last region (n_ranks %d)",
+                    static_cast<long long>(last), geom->n_ranks);
+    const int d = geom->rank - rank_start;
+    if (d < 0 || d % rank_stride != 0 || d / rank_stride >= W)
+        return fail(AG_ERR_INVALID_ARG, "rank %d is not a member of the group (start %d, stride %d, W %d)",
+                    geom->rank, rank_start, rank_stride, W);
+    *g_out = d / rank_stride;
+    return AG_OK;
+}
+
+// Tuning constants of the copy kernel.
+#ifndef AG_COPY_MAX_SLICES
+#define AG_COPY_MAX_SLICES 4
+#endif
+constexpr int kCopyMaxVpt = 8;
+constexpr int kCopyMaxSlices = AG_COPY_MAX_SLICES;
+
+}  // namespace
+
+extern "C" {
+
+const char* ag_status_string(ag_status_t s)
+{
+    switch (s) {
+    case AG_OK: return "AG_OK";
+    case AG_ERR_INVALID_ARG: return "AG_ERR_INVALID_ARG";
+    case AG_ERR_UNSUPPORTED: return "AG_ERR_UNSUPPORTED";
+    case AG_ERR_OUT_OF_MEMORY: return "AG_ERR_OUT_OF_MEMORY";
+    case AG_ERR_HIP: return "AG_ERR_HIP";
+    default: return "AG_ERR_UNKNOWN";
+    }
+}
+
+const char* ag_last_error_message(void) { return g_last_error.c_str(); }
+
+const char* ag_version(void) { return "libag 0.1 (gfx950)"; }
+
+ag_status_t ag_heap_create(int n_ranks, size_t bytes_per_rank, ag_heap_t** out)
+{
+    if (!out) return fail(AG_ERR_INVALID_ARG, "out is NULL");
+    if (n_ranks < 1 || n_ranks > 1024) return fail(AG_ERR_INVALID_ARG, "n_ranks %d not in [1, 1024]", n_ranks);
+    if (bytes_per_rank == 0) return fail(AG_ERR_INVALID_ARG, "bytes_per_rank is 0");
+    const uint64_t S = ceil_div(bytes_per_rank, AG_REGION_ALIGN) * AG_REGION_ALIGN;
+    if (S / AG_REGION_ALIGN > (uint64_t{1} << 40) / static_cast<uint64_t>(n_ranks))
+        return fail(AG_ERR_INVALID_ARG, "heap size overflows");
+    auto core = std::make_shared<HeapCore>();
+    core->n_ranks = n_ranks;
+    core->bytes_per_rank = S;
+    core->owns_slab = true;
+    const hipError_t e = hipMalloc(&core->slab, S * static_cast<uint64_t>(n_ranks));
+    if (e != hipSuccess) {
+        core->slab = nullptr;
+        return fail_hip(e, "hipMalloc(slab)");
+    }
+    return finish_heap(std::move(core), out);
+}
+
+ag_status_t ag_heap_wrap(void* dev_slab, int n_ranks, size_t bytes_per_rank, ag_heap_t** out)
+{
+    if (!out) return fail(AG_ERR_INVALID_ARG, "out is NULL");
+    if (!dev_slab || reinterpret_cast<uint64_t>(dev_slab) % 256 != 0)
+        return fail(AG_ERR_INVALID_ARG, "dev_slab is NULL or not 256-byte aligned");
+    if (n_ranks < 1 || n_ranks > 1024) return fail(AG_ERR_INVALID_ARG, "n_ranks %d not in [1, 1024]", n_ranks);
+    if (bytes_per_rank == 0 || bytes_per_rank % 256 != 0)
+        return fail(AG_ERR_INVALID_ARG, "bytes_per_rank %zu is not a positive multiple of 256", bytes_per_rank);
+    auto core = std::make_shared<HeapCore>();
+    core->slab = dev_slab;
+    core->n_ranks = n_ranks;
+    core->bytes_per_rank = bytes_per_rank;
+    core->owns_slab = false;
+    return finish_heap(std::move(core), out);
+}
+
+ag_status_t ag_heap_view(const ag_heap_t* heap, int rank, ag_heap_t** view)
+{
+    if (!heap || !view) return fail(AG_ERR_INVALID_ARG, "heap or view is NULL");
+    if (rank < 0 || rank >= heap->core->n_ranks)
+        return fail(AG_ERR_INVALID_ARG, "rank %d not in [0, %d)", rank, heap->core->n_ranks);
+    auto* v = new (std::nothrow) ag_heap;
+    if (!v) return fail(AG_ERR_OUT_OF_MEMORY, "host allocation of the view failed");
+    v->core = heap->core;
+    v->rank = rank;
+    *view = v;
+    return ok();
+}
+
+ag_status_t ag_heap_destroy(ag_heap_t* heap)
+{
+    delete heap;   // the shared state goes with its last handle
+    return ok();
+}
+
+ag_status_t ag_heap_alloc(ag_heap_t* heap, size_t bytes, size_t align, size_t* offset)
+{
+    if (!heap || !offset) return fail(AG_ERR_INVALID_ARG, "heap or offset is NULL");
+    if (align == 0) align = 256;
+    if (!is_pow2(align) || align < 256) return fail(AG_ERR_INVALID_ARG, "align %zu is not a power of two >= 256", align);
+    HeapCore& c = *heap->core;
+    std::lock_guard<std::mutex> lock(c.mu);
+    const uint64_t off = ceil_div(c.bump, align) * align;
+    if (off > c.bytes_per_rank || bytes > c.bytes_per_rank - off)
+        return fail(AG_ERR_OUT_OF_MEMORY, "symmetric heap exhausted: %zu bytes at offset %llu, region %llu bytes",
+                    bytes, static_cast<unsigned long long>(off), static_cast<unsigned long long>(c.bytes_per_rank));
+    c.bump = off + bytes;
+    *offset = off;
+    return ok();
+}
+
+ag_status_t ag_heap_reset(ag_heap_t* heap)
+{
+    if (!heap) return fail(AG_ERR_INVALID_ARG, "heap is NULL");
+    std::lock_guard<std::mutex> lock(heap->core->mu);
+    heap->core->bump = 0;
+    return ok();
+}
+
+ag_status_t ag_heap_rank_ptr(const ag_heap_t* heap, int rank, size_t offset, void** dev_ptr)
+{
+    if (!heap || !dev_ptr) return fail(AG_ERR_INVALID_ARG, "heap or dev_ptr is NULL");
+    const HeapCore& c = *heap->core;
+    if (rank < 0 || rank >= c.n_ranks) return fail(AG_ERR_INVALID_ARG, "rank %d not in [0, %d)", rank, c.n_ranks);
+    if (offset > c.bytes_per_rank) return fail(AG_ERR_INVALID_ARG, "offset %zu past the region", offset);
+    *dev_ptr = static_cast<char*>(c.slab) + static_cast<uint64_t>(rank) * c.bytes_per_rank + offset;
+    return ok();
+}
+
+ag_status_t ag_heap_base_table(const ag_heap_t* heap, const uint64_t** dev_table)
+{
+    if (!heap || !dev_table) return fail(AG_ERR_INVALID_ARG, "heap or dev_table is NULL");
+    *dev_table = heap->core->table;
+    return ok();
+}
+
+ag_status_t ag_heap_geometry(const ag_heap_t* heap, ag_heap_geometry_t* geom)
+{
+    if (!heap || !geom) return fail(AG_ERR_INVALID_ARG, "heap or geom is NULL");
+    const HeapCore& c = *heap->core;
+    geom->slab_addr = reinterpret_cast<uint64_t>(c.slab);
+    geom->bytes_per_rank = c.bytes_per_rank;
+    geom->n_ranks = c.n_ranks;
+    geom->rank = heap->rank;
+    geom->num_cus = c.num_cus;
+    geom->reserved = 0;
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// all-gather
+// ---------------------------------------------------------------------------
+
+ag_status_t ag_plan_all_gather(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
+                               uint64_t input_addr, size_t out_offset, int64_t M_local, int64_t N,
+                               ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, ag_plan_t* plan)
+{
+    ag_status_t s = check_geometry(geom);
+    if (s != AG_OK) return s;
+    if (!plan) return fail(AG_ERR_INVALID_ARG, "plan is NULL");
+    int g = 0;
+    s = check_group(geom, W, rank_start, rank_stride, &g);
+    if (s != AG_OK) return s;
+    const int e = elem_bytes(dtype);
+    if (e == 0) return fail(AG_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    if (M_local < 0) return fail(AG_ERR_INVALID_ARG, "M_local %lld < 0", static_cast<long long>(M_local));
+    if (N < 1) return fail(AG_ERR_INVALID_ARG, "N %lld < 1", static_cast<long long>(N));
+    if (M_local > (int64_t{1} << 31) - 1 || N > (int64_t{1} << 31) - 1)
+        return fail(AG_ERR_UNSUPPORTED, "M_local or N >= 2^31");
+    if (n_programs < 0) return fail(AG_ERR_INVALID_ARG, "n_programs %d < 0", n_programs);
+    if (tile_m == 0 && tile_n == 0) {
+        tile_m = 8;
+        tile_n = 256;
+    } else if (tile_m <= 0 || tile_n <= 0) {
+        return fail(AG_ERR_INVALID_ARG, "tile %dx%d: give both sides, or 0,0 for the 8x256 default", tile_m, tile_n);
+    }
+    if (!is_pow2(tile_m) || !is_pow2(tile_n) || tile_m > 256 || tile_n < 8 || tile_n > 4096)
+        return fail(AG_ERR_UNSUPPORTED, "tile %dx%d: tile_m must be a power of two <= 256 and tile_n a power of two in [8, 4096]",
+                    tile_m, tile_n);
+    const uint64_t row_bytes = static_cast<uint64_t>(N) * e;
+    const uint64_t blk = static_cast<uint64_t>(M_local) * row_bytes;
+    if (out_offset % e != 0)
+        return fail(AG_ERR_INVALID_ARG, "out_offset %zu is not a multiple of the element size %d", out_offset, e);
+    if (blk > geom->bytes_per_rank / W || out_offset > geom->bytes_per_rank - W * blk)
+        return fail(AG_ERR_INVALID_ARG, "output block (%d x %llu bytes at offset %zu) exceeds the region (%llu bytes)",
+                    W, static_cast<unsigned long long>(blk), out_offset,
+                    static_cast<unsigned long long>(geom->bytes_per_rank));
+
+    ag_plan_t p{};
+    p.group_rank = g;
+    p.tile_m = tile_m;
+    p.tile_n = tile_n;
+    p.threads = 256;
+    p.rank_block_offset = out_offset + static_cast<uint64_t>(g) * blk;
+    p.bytes_read = blk;
+    p.bytes_written = blk * W;
+    if (M_local == 0) {   // nothing to move: valid no-op
+        *plan = p;
+        return ok();
+    }
+    if (input_addr == 0) return fail(AG_ERR_INVALID_ARG, "input is NULL");
+    if (input_addr % e != 0) return fail(AG_ERR_INVALID_ARG, "input is not aligned to the element size");
+
+    // input must not overlap any member's output block, except being exactly
+    // this rank's own rows in its own region
+    const uint64_t own = geom->slab_addr + static_cast<uint64_t>(geom->rank) * geom->bytes_per_rank + p.rank_block_offset;
+    if (input_addr != own) {
+        for (int j = 0; j < W; ++j) {
+            const uint64_t region = geom->slab_addr +
+                static_cast<uint64_t>(rank_start + j * rank_stride) * geom->bytes_per_rank;
+            if (overlaps(input_addr, blk, region + out_offset, W * blk))
+                return fail(AG_ERR_INVALID_ARG, "input overlaps the output block of region %d", rank_start + j * rank_stride);
+        }
+    }
+
+    // widest vector that every row start, the input and every output block allow
+    const uint64_t out_addr = geom->slab_addr + p.rank_block_offset;   // same alignment in every region
+    int vec = 16;
+    while (vec > e && ((row_bytes % vec) != 0 || (input_addr % vec) != 0 || (out_addr % vec) != 0)) vec /= 2;
+    const uint64_t tile_row_bytes = static_cast<uint64_t>(tile_n) * e;
+    const uint64_t tile_vecs = static_cast<uint64_t>(tile_m) * tile_row_bytes / vec;
+    if (tile_vecs % 256 != 0 || tile_vecs / 256 > kCopyMaxVpt)
+        return fail(AG_ERR_UNSUPPORTED, "tile %dx%d holds %llu %d-byte vectors; 256 to %d are supported",
+                    tile_m, tile_n, static_cast<unsigned long long>(tile_vecs), vec, 256 * kCopyMaxVpt);
+    if (static_cast<uint64_t>(tile_m) * row_bytes >= (uint64_t{1} << 31))
+        return fail(AG_ERR_UNSUPPORTED, "a tile spans 2 GiB or more of the input");
+
+    const uint64_t tiles_m = ceil_div(M_local, tile_m);
+    const uint64_t tiles_n = ceil_div(N, tile_n);
+    const uint64_t total = tiles_m * tiles_n;
+    if (total >= (uint64_t{1} << 31)) return fail(AG_ERR_UNSUPPORTED, "more than 2^31 tiles");
+
+    const uint64_t programs = n_programs == 0 ? geom->num_cus : n_programs;
+    // concurrent tiles per program: up to kCopyMaxSlices while every slice still gets a tile
+    uint64_t slices = 1;
+    while (slices < static_cast<uint64_t>(kCopyMaxSlices) && programs * slices * 2 <= total) slices *= 2;
+    const uint64_t grid = std::min<uint64_t>(programs, ceil_div(total, slices));
+
+    p.vec_bytes = vec;
+    p.vectors_per_thread = static_cast<int32_t>(tile_vecs / 256);
+    p.tiles_m = static_cast<int64_t>(tiles_m);
+    p.tiles_n = static_cast<int64_t>(tiles_n);
+    p.total_tiles = static_cast<int64_t>(total);
+    p.n_programs = static_cast<int32_t>(grid);
+    p.threads = static_cast<int32_t>(256 * slices);
+    *plan = p;
+    return ok();
+}
+
+ag_status_t ag_all_gather(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                          const void* input, size_t out_offset, int64_t M_local, int64_t N,
+                          ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, void* stream)
+{
+    if (!heap) return fail(AG_ERR_INVALID_ARG, "heap is NULL");
+    ag_heap_geometry_t geom;
+    ag_heap_geometry(heap, &geom);
+    ag_plan_t p;
+    ag_status_t s = ag_plan_all_gather(&geom, W, rank_start, rank_stride, reinterpret_cast<uint64_t>(input),
+                                       out_offset, M_local, N, dtype, tile_m, tile_n, n_programs, &p);
+    if (s != AG_OK) return s;
+    if (p.total_tiles == 0) return ok();
+    const int e = elem_bytes(dtype);
+    ag::CopyLaunch l{};
+    l.args.heap_bases = heap->core->table;
+    l.args.input = static_cast<const uint8_t*>(input);
+    l.args.rank_block_offset = p.rank_block_offset;
+    l.args.row_bytes = static_cast<uint64_t>(N) * e;
+    l.args.rows = static_cast<uint32_t>(M_local);
+    l.args.tile_m = static_cast<uint32_t>(p.tile_m);
+    l.args.tile_row_bytes = static_cast<uint32_t>(p.tile_n) * e;
+    l.args.vecs_per_row_log2 = static_cast<uint32_t>(log2_exact(static_cast<uint64_t>(p.tile_n) * e / p.vec_bytes));
+    l.args.tiles_n = static_cast<uint32_t>(p.tiles_n);
+    l.args.total_tiles = static_cast<uint32_t>(p.total_tiles);
+    l.args.rank = geom.rank;
+    l.args.rank_start = rank_start;
+    l.args.rank_stride = rank_stride;
+    l.args.group_rank = p.group_rank;
+    l.args.slices = static_cast<uint32_t>(p.threads / 256);
+    l.vec_bytes = p.vec_bytes;
+    l.world = W;
+    l.vpt = p.vectors_per_thread;
+    l.grid = p.n_programs;
+    const hipError_t e2 = ag::launch_copy(l, static_cast<hipStream_t>(stream));
+    if (e2 != hipSuccess) return fail_hip(e2, "all-gather kernel launch");
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// fused GEMM + all-gather
+// ---------------------------------------------------------------------------
+
+ag_status_t ag_plan_gemm_all_gather(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
+                                    uint64_t a_addr, int64_t lda, uint64_t b_addr, int64_t ldb,
+                                    size_t out_offset, int64_t M_local, int64_t N, int64_t K,
+                                    ag_dtype_t dtype, int tile_m, int tile_n, int tile_k,
+                                    int n_programs, ag_plan_t* plan)
+{
+    ag_status_t s = check_geometry(geom);
+    if (s != AG_OK) return s;
+    if (!plan) return fail(AG_ERR_INVALID_ARG, "plan is NULL");
+    int g = 0;
+    s = check_group(geom, W, rank_start, rank_stride, &g);
+    if (s != AG_OK) return s;
+    if (dtype == AG_F32) return fail(AG_ERR_UNSUPPORTED, "the fused GEMM takes fp16 or bf16 operands");
+    if (dtype != AG_F16 && dtype != AG_BF16) return fail(AG_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    if (M_local < 0) return fail(AG_ERR_INVALID_ARG, "M_local %lld < 0", static_cast<long long>(M_local));
+    if (N < 1) return fail(AG_ERR_INVALID_ARG, "N %lld < 1", static_cast<long long>(N));
+    if (K < 1) return fail(AG_ERR_INVALID_ARG, "K %lld < 1", static_cast<long long>(K));
+    if (n_programs < 0) return fail(AG_ERR_INVALID_ARG, "n_programs %d < 0", n_programs);
+    if (M_local > (int64_t{1} << 30) || N > (int64_t{1} << 30) || K > (int64_t{1} << 30))
+        return fail(AG_ERR_UNSUPPORTED, "M_local, N or K > 2^30");
+    if (K % 64 != 0) return fail(AG_ERR_UNSUPPORTED, "K %lld is not a multiple of 64", static_cast<long long>(K));
+    if (N % 8 != 0) return fail(AG_ERR_UNSUPPORTED, "N %lld is not a multiple of 8", static_cast<long long>(N));
+    if (lda < K || ldb < K) return fail(AG_ERR_INVALID_ARG, "lda %lld or ldb %lld < K %lld",
+                                        static_cast<long long>(lda), static_cast<long long>(ldb), static_cast<long long>(K));
+    if (lda % 8 != 0 || ldb % 8 != 0) return fail(AG_ERR_UNSUPPORTED, "lda and ldb must be multiples of 8");
+    if (out_offset % 16 != 0) return fail(AG_ERR_UNSUPPORTED, "out_offset %zu is not a multiple of 16", out_offset);
+    const uint64_t row_bytes = static_cast<uint64_t>(N) * 2;
+    const uint64_t blk = static_cast<uint64_t>(M_local) * row_bytes;
+    if (blk > geom->bytes_per_rank / W || out_offset > geom->bytes_per_rank - W * blk)
+        return fail(AG_ERR_INVALID_ARG, "output block (%d x %llu bytes at offset %zu) exceeds the region (%llu bytes)",
+                    W, static_cast<unsigned long long>(blk), out_offset,
+                    static_cast<unsigned long long>(geom->bytes_per_rank));
+    int tile = 0;
+    if (tile_m == 0 && tile_n == 0 && tile_k == 0) {
+        const uint64_t big = ceil_div(M_local, 256) * ceil_div(N, 256);
+        tile = big >= static_cast<uint64_t>(geom->num_cus) ? 256 : 128;
+    } else if (tile_m == 256 && tile_n == 256 && tile_k == 64) {
+        tile = 256;
+    } else if (tile_m == 128 && tile_n == 128 && tile_k == 64) {
+        tile = 128;
+    } else {
+        return fail(AG_ERR_UNSUPPORTED, "tile %dx%dx%d: supported are 256x256x64 and 128x128x64 (0,0,0 = choose)",
+                    tile_m, tile_n, tile_k);
+    }
+
+    ag_plan_t p{};
+    p.group_rank = g;
+    p.tile_m = tile;
+    p.tile_n = tile;
+    p.tile_k = 64;
+    p.vec_bytes = 16;
+    p.rank_block_offset = out_offset + static_cast<uint64_t>(g) * blk;
+    p.bytes_read = (static_cast<uint64_t>(M_local) + static_cast<uint64_t>(N)) * static_cast<uint64_t>(K) * 2;
+    p.bytes_written = blk * W;
+    p.flops = 2.0 * static_cast<double>(M_local) * static_cast<double>(N) * static_cast<double>(K);
+    if (M_local == 0) {
+        p.bytes_read = 0;
+        *plan = p;
+        return ok();
+    }
+    if (a_addr == 0 || b_addr == 0) return fail(AG_ERR_INVALID_ARG, "A or B is NULL");
+    if (a_addr % 16 != 0 || b_addr % 16 != 0) return fail(AG_ERR_UNSUPPORTED, "A and B must be 16-byte aligned");
+    const uint64_t a_bytes = (static_cast<uint64_t>(M_local - 1) * lda + K) * 2;
+    const uint64_t b_bytes = (static_cast<uint64_t>(N - 1) * ldb + K) * 2;
+    for (int j = 0; j < W; ++j) {
+        const uint64_t region = geom->slab_addr + static_cast<uint64_t>(rank_start + j * rank_stride) * geom->bytes_per_rank;
+        if (overlaps(a_addr, a_bytes, region + out_offset, W * blk) ||
+            overlaps(b_addr, b_bytes, region + out_offset, W * blk))
+            return fail(AG_ERR_INVALID_ARG, "A or B overlaps the output block of region %d", rank_start + j * rank_stride);
+    }
+    if (static_cast<uint64_t>(tile) * row_bytes >= (uint64_t{1} << 31) || a_bytes >= (uint64_t{1} << 31) * 2 ||
+        blk >= (uint64_t{1} << 32))
+        return fail(AG_ERR_UNSUPPORTED, "operand or output block too large for 32-bit buffer offsets");
+    const uint64_t tiles_m = ceil_div(M_local, tile);
+    const uint64_t tiles_n = ceil_div(N, tile);
+    const uint64_t total = tiles_m * tiles_n;
+    const uint64_t programs = n_programs == 0 ? geom->num_cus : n_programs;
+    p.tiles_m = static_cast<int64_t>(tiles_m);
+    p.tiles_n = static_cast<int64_t>(tiles_n);
+    p.total_tiles = static_cast<int64_t>(total);
+    p.n_programs = static_cast<int32_t>(std::min<uint64_t>(programs, total));
+    p.threads = 256;
+    p.lds_bytes = 0;
+    *plan = p;
+    return ok();
+}
+
+ag_status_t ag_gemm_all_gather(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                               const void* A, int64_t lda, const void* B, int64_t ldb,
+                               size_t out_offset, int64_t M_local, int64_t N, int64_t K,
+                               ag_dtype_t dtype, int tile_m, int tile_n, int tile_k,
+                               int n_programs, void* stream)
+{
+    if (!heap) return fail(AG_ERR_INVALID_ARG, "heap is NULL");
+    ag_heap_geometry_t geom;
+    ag_heap_geometry(heap, &geom);
+    ag_plan_t p;
+    ag_status_t s = ag_plan_gemm_all_gather(&geom, W, rank_start, rank_stride, reinterpret_cast<uint64_t>(A), lda,
+                                            reinterpret_cast<uint64_t>(B), ldb, out_offset, M_local, N, K, dtype,
+                                            tile_m, tile_n, tile_k, n_programs, &p);
+    if (s != AG_OK) return s;
+    if (p.total_tiles == 0) return ok();
+    ag::GemmLaunch l{};
+    l.args.heap_bases = heap->core->table;
+    l.args.A = static_cast<const uint16_t*>(A);
+    l.args.B = static_cast<const uint16_t*>(B);
+    l.args.rank_block_offset = p.rank_block_offset;
+    l.args.lda = lda;
+    l.args.ldb = ldb;
+    l.args.M = static_cast<int32_t>(M_local);
+    l.args.N = static_cast<int32_t>(N);
+    l.args.K = static_cast<int32_t>(K);
+    l.args.tiles_m = static_cast<int32_t>(p.tiles_m);
+    l.args.tiles_n = static_cast<int32_t>(p.tiles_n);
+    l.args.total_tiles = static_cast<int32_t>(p.total_tiles);
+    l.args.rank = geom.rank;
+    l.args.rank_start = rank_start;
+    l.args.rank_stride = rank_stride;
+    l.args.group_rank = p.group_rank;
+    l.bf16 = dtype == AG_BF16 ? 1 : 0;
+    l.world = W;
+    l.tile = p.tile_m;
+    l.grid = p.n_programs;
+    l.threads = p.threads;
+    l.lds_bytes = p.lds_bytes;
+    const hipError_t e = ag::launch_gemm(l, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return fail(AG_ERR_UNSUPPORTED, "fused GEMM kernel variant not available");
+    if (e != hipSuccess) return fail_hip(e, "fused GEMM kernel launch");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,229 @@
+/*
+ * ag.h -- C ABI of libag: a symmetric heap of logical ranks on one MI355X
+ * (gfx950), a persistent tiled multi-destination all-gather, and a tiled
+ * GEMM whose epilogue performs the same multi-destination store.
+ *
+ * Sources (the three pages on the iris all-gather):
+ *  - ROCm/iris #626, "Summary": the device-side all-gather loads the local
+ *    and every peer heap base once, before the first store, keeps each peer
+ *    as a pointer delta (peer_base - local_base), stores the local copy
+ *    first and then the peers in rotated order (rank+1, rank+2, ...).
+ *  - ROCm/iris #626, "Triton CCL all-gather": the persistent kernel walks
+ *    tiles with a grid stride and translates the output base once per peer
+ *    before the tile loop.
+ *  - ROCm/iris #626, "Assembly" table: the fused matmul + all-gather kernel
+ *    stores its 256x256 fp16 C tile to every rank, with the heap-base loads
+ *    hoisted above the K loop.
+ *  - ROCm/iris #594, "Multi-GPU CI" / "Local validation": the result is that
+ *    of torch.distributed.all_gather_into_tensor; logical ranks may be
+ *    independent regions of memory on one GPU.
+ *  - ROCm/iris #591, "Hoist the peer heap bases": groups are described by
+ *    (rank_start, rank_stride, world_size); heap_bases is a device array of
+ *    every rank's heap base.
+ *
+ * Conventions shared by every entry point
+ *  - All pointers named dev_* or passed as input/A/B are device addresses in
+ *    the current HIP device's memory; host pointers are named out/plan/etc.
+ *  - Every entry point returns ag_status_t.  On any status other than AG_OK
+ *    nothing was launched and no output argument was written, and
+ *    ag_last_error_message() gives a one-line reason (thread-local).
+ *  - Launching entry points are asynchronous and ordered on the given
+ *    hipStream_t (NULL = the null stream).  They never synchronise.  A launch
+ *    failure reported by the runtime returns AG_ERR_HIP.
+ *  - Argument validation is done on the host before any HIP call; values are
+ *    never remapped: 0 means "documented default", anything else is used as
+ *    given or rejected.
+ */
+#ifndef AG_H
+#define AG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ag_status {
+    AG_OK = 0,
+    AG_ERR_INVALID_ARG = 1,   /* an argument is out of range, misaligned, null or overlapping */
+    AG_ERR_UNSUPPORTED = 2,   /* valid request this library does not implement (e.g. W > 8) */
+    AG_ERR_OUT_OF_MEMORY = 3, /* device allocation failed or the symmetric heap is exhausted */
+    AG_ERR_HIP = 4            /* a HIP runtime call failed (no device, launch error, ...) */
+} ag_status_t;
+
+typedef enum ag_dtype {
+    AG_F16 = 0,   /* IEEE binary16, 2 bytes */
+    AG_BF16 = 1,  /* bfloat16, 2 bytes */
+    AG_F32 = 2    /* IEEE binary32, 4 bytes (all-gather only) */
+} ag_dtype_t;
+
+/* Largest group the kernels are instantiated for (destination loop is a static unroll). */
+#define AG_MAX_WORLD 8
+/* Alignment of every region stride created by ag_heap_create. */
+#define AG_REGION_ALIGN ((size_t)2 << 20)
+
+typedef struct ag_heap ag_heap_t;  /* opaque */
+
+/* Where a heap lives; filled by ag_heap_geometry, or by hand for planning only. */
+typedef struct ag_heap_geometry {
+    uint64_t slab_addr;       /* device address of region 0 (region r = slab_addr + r*bytes_per_rank) */
+    uint64_t bytes_per_rank;  /* region stride in bytes, a multiple of 256 */
+    int32_t n_ranks;          /* number of regions, >= 1 */
+    int32_t rank;             /* calling rank of a view, or -1 for the root handle */
+    int32_t num_cus;          /* compute units of the heap's device (default n_programs) */
+    int32_t reserved;         /* must be 0 */
+} ag_heap_geometry_t;
+
+/* What a call will launch: filled by the ag_plan_* functions (pure host logic). */
+typedef struct ag_plan {
+    int32_t group_rank;          /* g = (rank - rank_start) / rank_stride */
+    int32_t vec_bytes;           /* bytes per vector access of the copy kernel (16/8/4/2) */
+    int32_t tile_m, tile_n, tile_k; /* effective tile (tile_k = 0 for the all-gather) */
+    int32_t n_programs;          /* persistent workgroups launched */
+    int32_t threads;             /* threads per workgroup */
+    int32_t lds_bytes;           /* LDS per workgroup */
+    int32_t vectors_per_thread;  /* copy kernel: vector accesses per thread per tile */
+    int32_t reserved;
+    int64_t tiles_m, tiles_n, total_tiles;
+    uint64_t rank_block_offset;  /* byte offset of this rank's rows inside every region (out_offset + g*M_local*N*e) */
+    uint64_t bytes_read;         /* algorithmic bytes read per call */
+    uint64_t bytes_written;      /* algorithmic bytes written per call (W destinations) */
+    double flops;                /* 2*M_local*N*K for the GEMM, 0 for the all-gather */
+} ag_plan_t;
+
+/* ------------------------------------------------------------------------
+ * Symmetric heap (ROCm/iris #626 "Summary" and #591: one heap per rank,
+ * tensors at the same offset in every heap, kernels read the device array
+ * heap_bases).  Here the n_ranks heaps are disjoint regions of one device
+ * allocation (ROCm/iris #594 "Local validation": logical ranks as separate
+ * memory on one GPU), and heap_bases[r] = slab + r*bytes_per_rank lives in
+ * a separate device array of n_ranks uint64_t.
+ * ------------------------------------------------------------------------ */
+
+/* Allocate a slab of n_ranks regions of bytes_per_rank bytes (rounded up to
+ * AG_REGION_ALIGN) plus the device base table, on the current device.  The
+ * heap owns both.  n_ranks in [1, 1024], bytes_per_rank >= 1.  Contents of
+ * the slab are undefined.  AG_ERR_OUT_OF_MEMORY if hipMalloc fails,
+ * AG_ERR_HIP if no device is usable. */
+ag_status_t ag_heap_create(int n_ranks, size_t bytes_per_rank, ag_heap_t** out);
+
+/* Build a heap over caller-owned device memory of n_ranks*bytes_per_rank
+ * bytes (e.g. a torch uint8 tensor).  dev_slab must be 256-byte aligned and
+ * bytes_per_rank a non-zero multiple of 256.  The library allocates and owns
+ * only the base table; the caller keeps the slab alive until every handle
+ * on it is destroyed. */
+ag_status_t ag_heap_wrap(void* dev_slab, int n_ranks, size_t bytes_per_rank, ag_heap_t** out);
+
+/* A handle for one calling rank ("the caller's rank", as the context object
+ * of iris knows its rank).  Views share the slab, the table and the
+ * allocator of the heap; the shared state lives until the last handle is
+ * destroyed. */
+ag_status_t ag_heap_view(const ag_heap_t* heap, int rank, ag_heap_t** view);
+
+/* Release a handle.  The caller must have synchronised every stream that
+ * uses the heap.  NULL is accepted and ignored. */
+ag_status_t ag_heap_destroy(ag_heap_t* heap);
+
+/* Symmetric bump allocation: returns a byte offset valid in every region.
+ * align must be a power of two >= 256 (0 = 256).  AG_ERR_OUT_OF_MEMORY when
+ * the region is exhausted.  Host-only; thread-safe per heap. */
+ag_status_t ag_heap_alloc(ag_heap_t* heap, size_t bytes, size_t align, size_t* offset);
+
+/* Forget every allocation (offsets restart at 0). */
+ag_status_t ag_heap_reset(ag_heap_t* heap);
+
+/* Device address of offset in region rank.  offset <= bytes_per_rank. */
+ag_status_t ag_heap_rank_ptr(const ag_heap_t* heap, int rank, size_t offset, void** dev_ptr);
+
+/* Device address of the uint64_t[n_ranks] base table the kernels read. */
+ag_status_t ag_heap_base_table(const ag_heap_t* heap, const uint64_t** dev_table);
+
+/* Geometry of a handle (host copy, no device access). */
+ag_status_t ag_heap_geometry(const ag_heap_t* heap, ag_heap_geometry_t* geom);
+
+/* ------------------------------------------------------------------------
+ * All-gather (ROCm/iris #626 "Summary" and "Triton CCL all-gather"; result
+ * defined by ROCm/iris #594 "Multi-GPU CI").
+ *
+ * heap          a view (ag_heap_view) of the calling rank
+ * W             group size, 1..AG_MAX_WORLD
+ * rank_start,
+ * rank_stride   group members are regions rank_start + j*rank_stride, j < W;
+ *               the view's rank must be one of them; g is its group index
+ * input         device pointer to M_local x N elements, row-major, ld = N
+ * out_offset    byte offset (multiple of the element size) of the gathered
+ *               W*M_local x N output inside every member region
+ * tile_m,tile_n tile of the persistent loop; 0,0 = 8x256.  Powers of two with
+ *               tile_n in [8, 4096], tile_m in [1, 256]; one tile must hold
+ *               between 1 and 16 vector accesses per thread of a 256-thread
+ *               workgroup at the vector width chosen (AG_ERR_UNSUPPORTED
+ *               otherwise)
+ * n_programs    persistent workgroups; 0 = number of CUs
+ * stream        hipStream_t
+ *
+ * After the call completes on stream, rows [g*M_local, (g+1)*M_local) of the
+ * output in every member region hold input; no other byte of the slab
+ * changes.  The input tile is read once and stored to the local region
+ * first, then to the peers in rotated group order (g+1, g+2, ... mod W).
+ * Calls for different ranks of a group write disjoint rows and may run
+ * concurrently on different streams.  M_local = 0 is a no-op.  input must
+ * not overlap any member's output block, except that it may be exactly this
+ * rank's own rows in its own region (in-place).
+ * ------------------------------------------------------------------------ */
+ag_status_t ag_all_gather(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                          const void* input, size_t out_offset, int64_t M_local, int64_t N,
+                          ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, void* stream);
+
+/* The validation and launch decisions of ag_all_gather for a heap
+ * geometry, without touching any device (input_addr is the device address
+ * as an integer).  Returns the status ag_all_gather would return before
+ * launching; fills *plan on AG_OK. */
+ag_status_t ag_plan_all_gather(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
+                               uint64_t input_addr, size_t out_offset, int64_t M_local, int64_t N,
+                               ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, ag_plan_t* plan);
+
+/* ------------------------------------------------------------------------
+ * Fused GEMM + all-gather (ROCm/iris #626 "Assembly" table and "Benchmark").
+ *
+ * C = A . B with fp32 accumulation, rounded once (nearest-even) to dtype,
+ * then stored exactly as ag_all_gather stores its input: rows
+ * [g*M_local, (g+1)*M_local) of the W*M_local x N output at out_offset in
+ * every member region, local region first, peers in rotated order.
+ *
+ * A             device, M_local x K, row-major, element (m,k) at A[m*lda + k], lda >= K
+ * B             device, K-contiguous: element (k,n) at B[n*ldb + k], ldb >= K
+ *               (the N x K row-major weight of a linear layer)
+ * dtype         AG_F16 or AG_BF16 (A, B and C share it); AG_F32 -> AG_ERR_UNSUPPORTED
+ * tile_m,tile_n,tile_k   0,0,0 = chosen by the library (256x256x64 when the
+ *               tile count fills the device, else 128x128x64); explicit
+ *               values must be one of 256x256x64, 128x128x64
+ * n_programs    persistent workgroups; 0 = number of CUs (capped at the tile count)
+ * Requirements: K a positive multiple of 64, lda/ldb multiples of 8, A, B
+ * 16-byte aligned, N*2 and out_offset multiples of 16 bytes.  M_local and N
+ * need not be tile multiples.  M_local = 0 is a no-op.  A and B must not
+ * overlap any member's output block.
+ * ------------------------------------------------------------------------ */
+ag_status_t ag_gemm_all_gather(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                               const void* A, int64_t lda, const void* B, int64_t ldb,
+                               size_t out_offset, int64_t M_local, int64_t N, int64_t K,
+                               ag_dtype_t dtype, int tile_m, int tile_n, int tile_k,
+                               int n_programs, void* stream);
+
+/* Host-only validation and launch decisions of ag_gemm_all_gather. */
+ag_status_t ag_plan_gemm_all_gather(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
+                                    uint64_t a_addr, int64_t lda, uint64_t b_addr, int64_t ldb,
+                                    size_t out_offset, int64_t M_local, int64_t N, int64_t K,
+                                    ag_dtype_t dtype, int tile_m, int tile_n, int tile_k,
+                                    int n_programs, ag_plan_t* plan);
+
+/* ------------------------------------------------------------------------ */
+const char* ag_status_string(ag_status_t status);  /* static string, never NULL */
+const char* ag_last_error_message(void);           /* thread-local; "" after AG_OK */
+const char* ag_version(void);                      /* static string */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AG_H */

@@ -1,0 +1,217 @@
+"""Host-side checks of libag with no GPU: exported symbols, validation and launch planning.
+
+The ag_plan_* entry points hold every validation and launch decision of
+ag_all_gather / ag_gemm_all_gather and touch no device, so they run here on
+hand-made heap geometries.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gemm_all_gather_amd import binding as ag
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ag.h")
+
+SLAB = 1 << 32
+MiB = 1 << 20
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ag_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert "ag_all_gather" in names and "ag_gemm_all_gather" in names and "ag_heap_create" in names
+    lib = ctypes.CDLL(ag.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert ag.version().startswith("libag")
+
+
+def test_status_strings():
+    lib = ag.lib()
+    for code, name in ag.STATUS_NAMES.items():
+        assert lib.ag_status_string(code).decode() == name
+    assert lib.ag_status_string(99).decode() == "AG_ERR_UNKNOWN"
+
+
+def geom(n_ranks=8, bytes_per_rank=64 * MiB, rank=0, num_cus=256, slab=SLAB):
+    return ag.Geometry(slab_addr=slab, bytes_per_rank=bytes_per_rank, n_ranks=n_ranks, rank=rank,
+                       num_cus=num_cus)
+
+
+INPUT = 1 << 44   # a device address far from the slab
+
+
+def plan(g=None, W=8, start=0, stride=1, inp=INPUT, off=0, M=1024, N=4096, dtype="f16", tm=0, tn=0, progs=0):
+    return ag.plan_all_gather(g or geom(), W, start, stride, inp, off, M, N, dtype, tm, tn, progs)
+
+
+def status_of(fn, *a, **k):
+    try:
+        fn(*a, **k)
+    except ag.AgError as exc:
+        return exc.status, exc.message
+    return ag.AG_OK, ""
+
+
+def test_plan_default_workload():
+    p = plan(g=geom(rank=3))
+    assert (p.tile_m, p.tile_n) == (8, 256)           # 0,0 is the documented 8x256 default
+    assert p.group_rank == 3
+    assert p.vec_bytes == 16 and p.vectors_per_thread == 1
+    assert p.tiles_m == 128 and p.tiles_n == 16 and p.total_tiles == 2048
+    assert p.rank_block_offset == 3 * 1024 * 4096 * 2
+    assert p.bytes_read == 1024 * 4096 * 2 and p.bytes_written == 8 * p.bytes_read
+    assert p.n_programs <= 256 and p.threads % 256 == 0
+
+
+def test_plan_explicit_tile_is_never_remapped():
+    for tm, tn in [(32, 64), (8, 256), (16, 128), (4, 512)]:
+        p = plan(tm=tm, tn=tn)
+        assert (p.tile_m, p.tile_n) == (tm, tn)
+
+
+def test_plan_strided_group_uses_group_rank():
+    p = plan(g=geom(rank=5), W=4, start=1, stride=2)
+    assert p.group_rank == 2
+    assert p.rank_block_offset == 2 * 1024 * 4096 * 2
+
+
+@pytest.mark.parametrize("N,dtype,inp,off,vec", [
+    (4096, "f16", INPUT, 0, 16), (4100, "f16", INPUT, 0, 8), (4098, "f16", INPUT, 0, 4),
+    (4097, "f16", INPUT, 0, 2), (4096, "f16", INPUT + 8, 0, 8), (4096, "f16", INPUT, 2, 2),
+    (4096, "f32", INPUT, 4, 4), (4097, "f32", INPUT, 0, 4), (4098, "f32", INPUT, 0, 8),
+])
+def test_plan_vector_width_follows_alignment(N, dtype, inp, off, vec):
+    p = plan(N=N, dtype=dtype, inp=inp, off=off, M=64)
+    assert p.vec_bytes == vec
+
+
+def test_plan_programs_and_tiles():
+    p = plan(M=64, N=256, progs=4)        # 8 tiles over 4 programs
+    assert p.total_tiles == 8 and p.n_programs * (p.threads // 256) <= 8
+    p = plan(M=1000, N=4100)              # partial tiles in both directions
+    assert p.tiles_m == 125 and p.tiles_n == 17
+    p = plan(M=8, N=256, progs=10_000)    # more programs than tiles: only one launched
+    assert p.n_programs == 1
+
+
+def test_plan_zero_rows_is_a_noop():
+    p = plan(M=0, inp=0)
+    assert p.total_tiles == 0 and p.n_programs == 0
+
+
+@pytest.mark.parametrize("over,status,text", [
+    (dict(W=0), ag.AG_ERR_INVALID_ARG, "W"),
+    (dict(W=9), ag.AG_ERR_UNSUPPORTED, "W"),
+    (dict(start=-1), ag.AG_ERR_INVALID_ARG, "rank_start"),
+    (dict(stride=0), ag.AG_ERR_INVALID_ARG, "rank_stride"),
+    (dict(W=4, start=1, stride=3), ag.AG_ERR_INVALID_ARG, "past the last region"),
+    (dict(W=4, start=1, stride=2), ag.AG_ERR_INVALID_ARG, "not a member"),    # rank 0 not in {1,3,5,7}
+    (dict(M=-1), ag.AG_ERR_INVALID_ARG, "M_local"),
+    (dict(N=0), ag.AG_ERR_INVALID_ARG, "N"),
+    (dict(off=1), ag.AG_ERR_INVALID_ARG, "element size"),
+    (dict(off=64 * MiB - 2), ag.AG_ERR_INVALID_ARG, "exceeds the region"),
+    (dict(M=1025), ag.AG_ERR_INVALID_ARG, "exceeds the region"),
+    (dict(tm=3, tn=256), ag.AG_ERR_UNSUPPORTED, "power of two"),
+    (dict(tm=8, tn=0), ag.AG_ERR_INVALID_ARG, "both sides"),
+    (dict(tm=512, tn=256), ag.AG_ERR_UNSUPPORTED, "power of two"),
+    (dict(tm=1, tn=256), ag.AG_ERR_UNSUPPORTED, "vectors"),                    # 32 vectors < 256
+    (dict(tm=64, tn=512), ag.AG_ERR_UNSUPPORTED, "vectors"),                   # 4096 vectors > 2048
+    (dict(progs=-1), ag.AG_ERR_INVALID_ARG, "n_programs"),
+    (dict(dtype=5), ag.AG_ERR_INVALID_ARG, "dtype"),
+    (dict(inp=0), ag.AG_ERR_INVALID_ARG, "NULL"),
+    (dict(inp=INPUT + 1), ag.AG_ERR_INVALID_ARG, "aligned"),
+])
+def test_plan_rejects(over, status, text):
+    kw = dict(over)
+    got, msg = status_of(plan, **kw)
+    assert got == status, (over, got, msg)
+    assert text in msg, msg
+
+
+def test_plan_rejects_bad_geometry_and_root_handle():
+    for g, text in [(geom(rank=-1), "not a view"), (geom(rank=8), "not a view"), (geom(n_ranks=0), "n_ranks"),
+                    (geom(bytes_per_rank=100), "multiple of 256"), (geom(slab=0), "slab"),
+                    (geom(num_cus=0), "num_cus")]:
+        got, msg = status_of(plan, g=g)
+        assert got == ag.AG_ERR_INVALID_ARG and text in msg, (msg,)
+
+
+def test_plan_input_overlap_rules():
+    S = 64 * MiB
+    blk = 1024 * 4096 * 2
+    g = geom(rank=2)
+    own = SLAB + 2 * S + 2 * blk
+    assert plan(g=g, inp=own).group_rank == 2                     # exactly its own slot: in place
+    got, msg = status_of(plan, g=g, inp=own + 2)                   # shifted: overlaps
+    assert got == ag.AG_ERR_INVALID_ARG and "overlaps" in msg
+    got, _ = status_of(plan, g=g, inp=SLAB + 5 * S + 7 * blk)      # inside another member's block
+    assert got == ag.AG_ERR_INVALID_ARG
+    assert plan(g=geom(rank=1), W=2, start=0, stride=1, inp=SLAB + 5 * S).group_rank == 1   # non-member region
+
+
+# ---------------------------------------------------------------------------
+# fused GEMM + all-gather planning
+# ---------------------------------------------------------------------------
+
+A_ADDR, B_ADDR = 1 << 44, 1 << 45
+
+
+def gplan(g=None, W=8, start=0, stride=1, a=A_ADDR, lda=8192, b=B_ADDR, ldb=8192, off=0, M=1024, N=3584,
+          K=8192, dtype="f16", tm=0, tn=0, tk=0, progs=0):
+    return ag.plan_gemm_all_gather(g or geom(bytes_per_rank=1 << 30), W, start, stride, a, lda, b, ldb, off,
+                                   M, N, K, dtype, tm, tn, tk, progs)
+
+
+def test_gemm_plan_default_tiles():
+    p = gplan()
+    assert (p.tile_m, p.tile_n, p.tile_k) == (128, 128, 64)       # 56 tiles of 256^2 cannot fill 256 CUs
+    assert p.total_tiles == 8 * 28
+    assert p.flops == 2.0 * 1024 * 3584 * 8192
+    p = gplan(M=16384)
+    assert (p.tile_m, p.tile_n) == (256, 256) and p.total_tiles == 64 * 14
+    assert p.n_programs == 256
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype="f32"), ag.AG_ERR_UNSUPPORTED),
+    (dict(K=100), ag.AG_ERR_UNSUPPORTED),
+    (dict(N=3585), ag.AG_ERR_UNSUPPORTED),
+    (dict(lda=8000), ag.AG_ERR_INVALID_ARG),
+    (dict(lda=8196), ag.AG_ERR_UNSUPPORTED),
+    (dict(tm=64, tn=64, tk=64), ag.AG_ERR_UNSUPPORTED),
+    (dict(off=8), ag.AG_ERR_UNSUPPORTED),
+    (dict(a=A_ADDR + 2), ag.AG_ERR_UNSUPPORTED),
+    (dict(a=0), ag.AG_ERR_INVALID_ARG),
+    (dict(W=9), ag.AG_ERR_UNSUPPORTED),
+    (dict(M=40000), ag.AG_ERR_INVALID_ARG),
+    (dict(a=SLAB + 256), ag.AG_ERR_INVALID_ARG),      # A inside an output block
+])
+def test_gemm_plan_rejects(over, status):
+    got, msg = status_of(gplan, **over)
+    assert got == status, (over, got, msg)
+
+
+def test_heap_create_without_device_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    got, msg = status_of(ag.Heap.create, 2, MiB)
+    assert got == ag.AG_ERR_HIP and "hip" in msg.lower()
+
+
+def test_heap_argument_validation_without_device():
+    assert status_of(ag.Heap.create, 0, MiB)[0] == ag.AG_ERR_INVALID_ARG
+    assert status_of(ag.Heap.create, 2, 0)[0] == ag.AG_ERR_INVALID_ARG
+    assert status_of(ag.Heap.wrap, 0, 2, MiB)[0] == ag.AG_ERR_INVALID_ARG
+    assert status_of(ag.Heap.wrap, 1 << 30, 2, 1000)[0] == ag.AG_ERR_INVALID_ARG
+    assert status_of(ag.Heap.wrap, (1 << 30) + 8, 2, MiB)[0] == ag.AG_ERR_INVALID_ARG
