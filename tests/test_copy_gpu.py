@@ -193,7 +193,7 @@ def test_library_owned_heap_create_and_alloc():
         table = torch.empty(R, dtype=torch.int64, device="cuda")
 
         class _T:
-            __cuda_array_interface__ = {"shape": (R,), "typestr": "<i8", "data": (heap.base_table(), True),
+            __cuda_array_interface__ = {"shape": (R,), "typestr": "<i8", "data": (heap.base_table(), False),
                                         "version": 3, "strides": None}
 
         table.copy_(torch.as_tensor(_T(), device="cuda"))
