@@ -44,13 +44,13 @@ class Plan(ctypes.Structure):
     _fields_ = [("group_rank", ctypes.c_int32), ("vec_bytes", ctypes.c_int32),
                 ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
                 ("n_programs", ctypes.c_int32), ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
-                ("vectors_per_thread", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("vectors_per_thread", ctypes.c_int32), ("variant", ctypes.c_int32),
                 ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("total_tiles", ctypes.c_int64),
                 ("rank_block_offset", ctypes.c_uint64), ("bytes_read", ctypes.c_uint64),
                 ("bytes_written", ctypes.c_uint64), ("flops", ctypes.c_double)]
 
     def as_dict(self) -> dict:
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 _lib: Optional[ctypes.CDLL] = None

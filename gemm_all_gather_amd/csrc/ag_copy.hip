@@ -36,9 +36,12 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// Cache-policy bits of the destination stores (0 = default policy).
+// Cache-policy bits of the destination stores.  Non-temporal (nt, bit 1):
+// the W written copies are not re-read by this kernel, and streaming them
+// measured ~40% faster than the default policy on a 75 MB/call workload and
+// equal on a 2.4 GB/call one.
 #ifndef AG_COPY_STORE_AUX
-#define AG_COPY_STORE_AUX 0
+#define AG_COPY_STORE_AUX 2
 #endif
 
 // Word 3 of a raw (stride 0) buffer descriptor on gfx9-family parts:

@@ -161,9 +161,10 @@ ag_status_t check_group(const ag_heap_geometry_t* geom, int W, int rank_start, i
     return AG_OK;
 }
 
-// Tuning constants of the copy kernel.
+// Tuning constants of the copy kernel: concurrent 256-thread tile slices per
+// workgroup (1 measured best or equal at 64-256 programs).
 #ifndef AG_COPY_MAX_SLICES
-#define AG_COPY_MAX_SLICES 4
+#define AG_COPY_MAX_SLICES 1
 #endif
 constexpr int kCopyMaxVpt = 8;
 constexpr int kCopyMaxSlices = AG_COPY_MAX_SLICES;
@@ -471,23 +472,36 @@ ag_status_t ag_plan_gemm_all_gather(const ag_heap_geometry_t* geom, int W, int r
         return fail(AG_ERR_INVALID_ARG, "output block (%d x %llu bytes at offset %zu) exceeds the region (%llu bytes)",
                     W, static_cast<unsigned long long>(blk), out_offset,
                     static_cast<unsigned long long>(geom->bytes_per_rank));
-    int tile = 0;
+    // tile configurations the kernel is instantiated for: {TM, TN}, K step 64
+    struct TileCfg { int tm, tn, id; };
+    static const TileCfg kTiles[] = {{256, 256, ag::kGemmTile256x256}, {256, 224, ag::kGemmTile256x224},
+                                     {128, 128, ag::kGemmTile128x128}};
+    const uint64_t programs_req = n_programs == 0 ? geom->num_cus : n_programs;
+    const TileCfg* cfg = nullptr;
     if (tile_m == 0 && tile_n == 0 && tile_k == 0) {
-        const uint64_t big = ceil_div(M_local, 256) * ceil_div(N, 256);
-        tile = big >= static_cast<uint64_t>(geom->num_cus) ? 256 : 128;
-    } else if (tile_m == 256 && tile_n == 256 && tile_k == 64) {
-        tile = 256;
-    } else if (tile_m == 128 && tile_n == 128 && tile_k == 64) {
-        tile = 128;
+        // fewest MFMA-cycles on the busiest program: rounds of tiles x tile area;
+        // ties go to the larger tile (less operand traffic per flop)
+        uint64_t best = ~uint64_t{0};
+        for (const TileCfg& t : kTiles) {
+            const uint64_t tiles = ceil_div(M_local > 0 ? M_local : 1, t.tm) * ceil_div(N, t.tn);
+            const uint64_t cost = ceil_div(tiles, programs_req) * static_cast<uint64_t>(t.tm) * t.tn;
+            if (cost < best) {
+                best = cost;
+                cfg = &t;
+            }
+        }
     } else {
-        return fail(AG_ERR_UNSUPPORTED, "tile %dx%dx%d: supported are 256x256x64 and 128x128x64 (0,0,0 = choose)",
-                    tile_m, tile_n, tile_k);
+        for (const TileCfg& t : kTiles)
+            if (tile_m == t.tm && tile_n == t.tn && tile_k == 64) cfg = &t;
+        if (!cfg)
+            return fail(AG_ERR_UNSUPPORTED,
+                        "tile %dx%dx%d: supported are 256x256x64, 256x224x64 and 128x128x64 (0,0,0 = choose)",
+                        tile_m, tile_n, tile_k);
     }
-
     ag_plan_t p{};
     p.group_rank = g;
-    p.tile_m = tile;
-    p.tile_n = tile;
+    p.tile_m = cfg->tm;
+    p.tile_n = cfg->tn;
     p.tile_k = 64;
     p.vec_bytes = 16;
     p.rank_block_offset = out_offset + static_cast<uint64_t>(g) * blk;
@@ -509,19 +523,22 @@ ag_status_t ag_plan_gemm_all_gather(const ag_heap_geometry_t* geom, int W, int r
             overlaps(b_addr, b_bytes, region + out_offset, W * blk))
             return fail(AG_ERR_INVALID_ARG, "A or B overlaps the output block of region %d", rank_start + j * rank_stride);
     }
-    if (static_cast<uint64_t>(tile) * row_bytes >= (uint64_t{1} << 31) || a_bytes >= (uint64_t{1} << 31) * 2 ||
-        blk >= (uint64_t{1} << 32))
-        return fail(AG_ERR_UNSUPPORTED, "operand or output block too large for 32-bit buffer offsets");
-    const uint64_t tiles_m = ceil_div(M_local, tile);
-    const uint64_t tiles_n = ceil_div(N, tile);
+    // per-tile buffer descriptors address at most one tile of rows with 32-bit offsets
+    if (static_cast<uint64_t>(cfg->tm) * lda * 2 >= (uint64_t{1} << 31) ||
+        static_cast<uint64_t>(cfg->tn) * ldb * 2 >= (uint64_t{1} << 31) ||
+        static_cast<uint64_t>(cfg->tm) * row_bytes >= (uint64_t{1} << 31))
+        return fail(AG_ERR_UNSUPPORTED, "a tile of rows spans 2 GiB or more");
+    const uint64_t tiles_m = ceil_div(M_local, cfg->tm);
+    const uint64_t tiles_n = ceil_div(N, cfg->tn);
     const uint64_t total = tiles_m * tiles_n;
-    const uint64_t programs = n_programs == 0 ? geom->num_cus : n_programs;
+    if (total >= (uint64_t{1} << 31)) return fail(AG_ERR_UNSUPPORTED, "more than 2^31 tiles");
     p.tiles_m = static_cast<int64_t>(tiles_m);
     p.tiles_n = static_cast<int64_t>(tiles_n);
     p.total_tiles = static_cast<int64_t>(total);
-    p.n_programs = static_cast<int32_t>(std::min<uint64_t>(programs, total));
+    p.n_programs = static_cast<int32_t>(std::min<uint64_t>(programs_req, total));
     p.threads = 256;
-    p.lds_bytes = 0;
+    p.lds_bytes = 2 * (cfg->tm + cfg->tn) * 128;
+    p.variant = cfg->id;
     *plan = p;
     return ok();
 }
@@ -560,10 +577,8 @@ ag_status_t ag_gemm_all_gather(const ag_heap_t* heap, int W, int rank_start, int
     l.args.group_rank = p.group_rank;
     l.bf16 = dtype == AG_BF16 ? 1 : 0;
     l.world = W;
-    l.tile = p.tile_m;
+    l.cfg = p.variant;
     l.grid = p.n_programs;
-    l.threads = p.threads;
-    l.lds_bytes = p.lds_bytes;
     const hipError_t e = ag::launch_gemm(l, static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported) return fail(AG_ERR_UNSUPPORTED, "fused GEMM kernel variant not available");
     if (e != hipSuccess) return fail_hip(e, "fused GEMM kernel launch");

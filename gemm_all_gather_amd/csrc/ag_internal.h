@@ -49,14 +49,15 @@ struct GemmKernelArgs {
     int32_t rank, rank_start, rank_stride, group_rank;
 };
 
+// Tile configurations of the fused kernel (TM x TN, K step 64).
+enum GemmTile { kGemmTile256x256 = 0, kGemmTile256x224 = 1, kGemmTile128x128 = 2 };
+
 struct GemmLaunch {
     GemmKernelArgs args;
     int bf16;          // 0 = fp16, 1 = bf16
     int world;
-    int tile;          // 256 or 128 (square tiles, tile_k 64)
+    int cfg;           // GemmTile
     int grid;
-    int threads;
-    int lds_bytes;
 };
 
 hipError_t launch_gemm(const GemmLaunch& l, hipStream_t stream);

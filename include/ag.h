@@ -84,7 +84,7 @@ typedef struct ag_plan {
     int32_t threads;             /* threads per workgroup */
     int32_t lds_bytes;           /* LDS per workgroup */
     int32_t vectors_per_thread;  /* copy kernel: vector accesses per thread per tile */
-    int32_t reserved;
+    int32_t variant;             /* library-internal kernel variant (informational) */
     int64_t tiles_m, tiles_n, total_tiles;
     uint64_t rank_block_offset;  /* byte offset of this rank's rows inside every region (out_offset + g*M_local*N*e) */
     uint64_t bytes_read;         /* algorithmic bytes read per call */
@@ -195,9 +195,10 @@ ag_status_t ag_plan_all_gather(const ag_heap_geometry_t* geom, int W, int rank_s
  * B             device, K-contiguous: element (k,n) at B[n*ldb + k], ldb >= K
  *               (the N x K row-major weight of a linear layer)
  * dtype         AG_F16 or AG_BF16 (A, B and C share it); AG_F32 -> AG_ERR_UNSUPPORTED
- * tile_m,tile_n,tile_k   0,0,0 = chosen by the library (256x256x64 when the
- *               tile count fills the device, else 128x128x64); explicit
- *               values must be one of 256x256x64, 128x128x64
+ * tile_m,tile_n,tile_k   0,0,0 = chosen by the library: the configuration
+ *               with the fewest rounds-of-tiles x tile-area on the busiest
+ *               program (ties to the larger tile); explicit values must be
+ *               one of 256x256x64, 256x224x64, 128x128x64
  * n_programs    persistent workgroups; 0 = number of CUs (capped at the tile count)
  * Requirements: K a positive multiple of 64, lda/ldb multiples of 8, A, B
  * 16-byte aligned, N*2 and out_offset multiples of 16 bytes.  M_local and N

@@ -177,9 +177,11 @@ def test_gemm_plan_default_tiles():
     assert (p.tile_m, p.tile_n, p.tile_k) == (128, 128, 64)       # 56 tiles of 256^2 cannot fill 256 CUs
     assert p.total_tiles == 8 * 28
     assert p.flops == 2.0 * 1024 * 3584 * 8192
-    p = gplan(M=16384)
-    assert (p.tile_m, p.tile_n) == (256, 256) and p.total_tiles == 64 * 14
+    p = gplan(M=16384)                                             # 256x224: 64 x 16 tiles = 4 rounds of 256
+    assert (p.tile_m, p.tile_n) == (256, 224) and p.total_tiles == 64 * 16
     assert p.n_programs == 256
+    p = gplan(M=16384, tm=256, tn=256, tk=64)                      # explicit tiles are used as given
+    assert (p.tile_m, p.tile_n) == (256, 256) and p.total_tiles == 64 * 14
 
 
 @pytest.mark.parametrize("over,status", [
