@@ -5,8 +5,10 @@ One step = one complete logical all-gather job on one GPU:
     1024 x 4096 fp16 input (tile 8x256, 256 programs), so every heap region
     ends up with the 8192 x 4096 gathered tensor;
   * fused: every one of the 8 logical ranks calls ag_gemm_all_gather with
-    A_g 1024 x 8192 and the shared B 8192 x 3584 (fp16, fp32 accumulate), so
-    every region ends up with the 8192 x 3584 gathered C.
+    A_g 16384 x 8192 and the shared B 8192 x 3584 (fp16, fp32 accumulate),
+    so every region ends up with the 131072 x 3584 gathered C (the fused
+    workload whose MFMA-utilisation target is stated; --fused-m 1024 selects
+    the M_local = 1024 variant).
 Inputs are seeded synthetic tensors already resident in HBM.
 
 Printed: one JSON line.  value = all-gather HBM GB/s over the whole job
@@ -34,8 +36,9 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 
 # all-gather workload: W=8 logical ranks, 1024 x 4096 fp16 per rank
 AG_W, AG_M, AG_N, AG_DTYPE, AG_TILE, AG_PROGRAMS = 8, 1024, 4096, "f16", (8, 256), 256
-# fused workload: W=8, M_local 1024, K 8192, N 3584, fp16
-FU_W, FU_M, FU_N, FU_K, FU_DTYPE = 8, 1024, 3584, 8192, "f16"
+# fused workload: W=8, M_local 16384, K 8192, N 3584, fp16
+FU_W, FU_N, FU_K, FU_DTYPE = 8, 3584, 8192, "f16"
+FU_M = 16384
 
 
 def _src_hash(name: str) -> str:
@@ -110,13 +113,21 @@ def _cpu_baseline_fused(seconds: float):
 
 
 def main() -> int:
+    global FU_M
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused-m", type=int, default=FU_M, help="M_local of the fused workload (16384 or 1024)")
+    ap.add_argument("--only", choices=["all", "copy", "fused"], default="all",
+                    help="restrict the timed step to one kernel (profiling runs)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this many MiB "
+                         "(reference for HBM byte counters)")
     args = ap.parse_args()
+    FU_M = args.fused_m
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the W logical ranks are regions of one GPU's HBM; "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -149,6 +160,8 @@ def main() -> int:
     ag_plan = ag.plan_all_gather(geom, AG_W, 0, 1, ins[0], 0, AG_M, AG_N, AG_DTYPE, *AG_TILE, AG_PROGRAMS)
 
     def copy_job():
+        if args.only == "fused":
+            return
         for j in range(AG_W):
             ag.all_gather(views[j], AG_W, 0, 1, ins[j], 0, AG_M, AG_N, AG_DTYPE, AG_TILE[0], AG_TILE[1],
                           AG_PROGRAMS, stream)
@@ -162,6 +175,8 @@ def main() -> int:
     fu_off = S_ag
 
     def fused_job():
+        if args.only == "copy":
+            return
         for j in range(FU_W):
             ag.gemm_all_gather(views[j], FU_W, 0, 1, fa[j], FU_K, fb, FU_K, fu_off, FU_M, FU_N, FU_K, FU_DTYPE,
                                0, 0, 0, 0, stream)
@@ -195,6 +210,12 @@ def main() -> int:
         ev[k][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if args.calib_copy_mib > 0:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     copy_ms = sum(ev[k][0].elapsed_time(ev[k][1]) for k in range(args.steps)) / args.steps
     fused_ms = sum(ev[k][1].elapsed_time(ev[k][2]) for k in range(args.steps)) / args.steps
     step_ms = sum(ev[k][0].elapsed_time(ev[k][2]) for k in range(args.steps)) / args.steps

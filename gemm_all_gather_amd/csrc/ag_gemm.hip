@@ -97,48 +97,76 @@ struct Cfg {
     static constexpr int WGM = 2, WGN = 2;                 // wave grid
     static constexpr int WTM = TM / WGM, WTN = TN / WGN;   // wave sub-tile
     static constexpr int BM = WTM / 16, BN = WTN / 16;     // 16x16 blocks per wave
-    static constexpr int A_BYTES = TM * 128;               // one stage: TM rows x 64 K x 2 bytes
-    static constexpr int B_BYTES = TN * 128;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int A_LOADS = TM / 32;                // 1-KiB wave loads per wave per stage
-    static constexpr int B_LOADS = TN / 32;
+    static constexpr int NS = 4;                           // LDS ring slots
+    static constexpr int ROW_BYTES = 64;                   // one stage: K = 32 values of 2 bytes per row
+    static constexpr int A_BYTES = TM * ROW_BYTES;
+    static constexpr int STAGE = (TM + TN) * ROW_BYTES;
+    static constexpr int A_INSTR = TM / 16;                // 1-KiB wave loads (16 rows) per stage
+    static constexpr int B_INSTR = TN / 16;
+    static constexpr int INSTR = A_INSTR + B_INSTR;
+    static constexpr int A_J = A_INSTR / 4;                // loads j < A_J of every wave are A rows
+    static constexpr int MAXL = (INSTR + 3) / 4;           // loads per wave per stage (waves 0..)
     static constexpr int CPR = TN / 8;                     // 16-byte chunks per C row
     static constexpr bool XOR_SWIZZLE = (CPR & (CPR - 1)) == 0 && CPR >= 16;
     static constexpr int C_PITCH = XOR_SWIZZLE ? TN * 2 : TN * 2 + 16;
-    static constexpr int HALF_ROWS = TM / 2;               // C rows staged in each LDS stage
+    static constexpr int QROWS = TM / 4;                   // C rows staged in each ring slot
     static constexpr int CHUNKS_PER_THREAD = TM * CPR / 256;
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be made of 16x16 blocks");
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "stage loads move 8 rows per wave instruction");
-    static_assert(HALF_ROWS * C_PITCH <= STAGE, "C staging must fit in one stage");
-    static_assert((HALF_ROWS * CPR) % 256 == 0, "each LDS half must hold whole rounds of chunks");
-    static_assert(2 * STAGE <= 160 * 1024, "gfx950 has 160 KiB of LDS");
+    static_assert(TM % 64 == 0 && TN % 16 == 0, "stage loads move 16 rows per wave instruction");
+    static_assert(QROWS * C_PITCH <= STAGE, "a quarter of the C tile must fit in one ring slot");
+    static_assert((QROWS * CPR) % 256 == 0, "each ring slot must hold whole rounds of C chunks");
+    static_assert(WTM % QROWS == 0 || QROWS % 16 == 0, "wave rows map to whole ring slots per block row");
+    static_assert(NS * STAGE <= 160 * 1024, "gfx950 has 160 KiB of LDS");
 };
 }  // namespace gemm_cfg
 
 namespace {
 using gemm_cfg::Cfg;
 
-// One K stage (64 wide) of the A and B tiles, global -> LDS: each wave
-// instruction moves 8 rows x 128 bytes, lane l landing at byte 16*l of its
-// 1-KiB LDS block.  (A free function: the LDS pointer conversion and the
-// LDS-direct load are device-only.)
+// One K stage (32 wide) of the A and B tiles, global -> LDS.  Wave
+// instruction i of the stage moves 16 rows x 64 bytes (A rows for
+// i < A_INSTR, then B rows) to LDS bytes [i*1024, i*1024 + 1024) of the
+// slot; wave w issues instructions w, w+4, ...  A descriptor of size 0 turns
+// the loads of a stage past the end of K into no-ops that still count.
+// (Descriptors are passed as base + size: a template whose signature names
+// the buffer-resource type fails to substitute in the host compilation pass.)
+// ds_read_b128 of one 16-row fragment block at a compile-time offset.
+template <class C>
+struct Frag {
+    template <class V>
+    static __device__ __forceinline__ void read(V& dst, uint32_t addr, int block)
+    {
+        switch (block) {   // the offset must be an immediate
+#define AG_FRAG_CASE(b)                                                                                      \
+    case b:                                                                                                  \
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(b * 16 * C::ROW_BYTES)); \
+        break;
+            AG_FRAG_CASE(0) AG_FRAG_CASE(1) AG_FRAG_CASE(2) AG_FRAG_CASE(3)
+            AG_FRAG_CASE(4) AG_FRAG_CASE(5) AG_FRAG_CASE(6) AG_FRAG_CASE(7)
+#undef AG_FRAG_CASE
+        default: break;
+        }
+    }
+};
+
 template <class C>
 struct Stage {
     static __device__ __forceinline__ void load(uint64_t a_base, uint64_t a_records, uint64_t b_base,
-                                                uint64_t b_records, uint8_t* buf, int kt, int wave,
-                                                const uint32_t* a_voff, const uint32_t* b_voff)
+                                                uint64_t b_records, uint8_t* slot, int kt, int wave,
+                                                const uint32_t* voff)
     {
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, a_records);
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, b_records);
-        const uint32_t soff = static_cast<uint32_t>(kt) * 128u;   // k0 * 2 bytes
+        const uint32_t soff = static_cast<uint32_t>(kt) * 64u;   // k0 * 2 bytes
 #pragma unroll
-        for (int q = 0; q < C::A_LOADS; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (AG_LDS void*)(buf + (q * 4 + wave) * 1024), 16, a_voff[q],
-                                                     soff, 0, 0);
-#pragma unroll
-        for (int q = 0; q < C::B_LOADS; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (AG_LDS void*)(buf + C::A_BYTES + (q * 4 + wave) * 1024), 16,
-                                                     b_voff[q], soff, 0, 0);
+        for (int j = 0; j < C::MAXL; ++j) {
+            const int i = wave + 4 * j;
+            if (j < C::A_J) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (AG_LDS void*)(slot + i * 1024), 16, voff[j], soff, 0, 0);
+            } else if (i < C::INSTR) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (AG_LDS void*)(slot + i * 1024), 16, voff[j], soff, 0, 0);
+            }
+        }
     }
 };
 
@@ -147,8 +175,12 @@ __global__ __launch_bounds__(256) void ag_gemm_kernel(GemmKernelArgs a)
 {
     using M = Mfma<BF16>;
     using V = typename M::V;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::STAGE];
+    // four ring slots as separate objects, so the compiler can tell a read of
+    // one slot from an LDS-direct load still landing in another
+    __shared__ __attribute__((aligned(1024))) uint8_t ring0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring2[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring3[C::STAGE];
 
     // ---- destinations, translated once above the tile and K loops
     uint64_t base[W];
@@ -169,24 +201,28 @@ __global__ __launch_bounds__(256) void ag_gemm_kernel(GemmKernelArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WGN;
     const int wn = wave % C::WGN;
+    // loads per stage of this wave (MAXL or MAXL-1)
+    const bool full_share = wave + 4 * (C::MAXL - 1) < C::INSTR;
 
     // ---- tile-invariant lane offsets
     const uint32_t lda2 = static_cast<uint32_t>(a.lda) * 2u;
     const uint32_t ldb2 = static_cast<uint32_t>(a.ldb) * 2u;
-    const uint32_t swz_chunk = static_cast<uint32_t>((lane & 7) ^ (lane >> 3));   // XOR-swizzled 16-B chunk
-    uint32_t a_voff[C::A_LOADS], b_voff[C::B_LOADS];
+    const uint32_t lrow = static_cast<uint32_t>(lane >> 2);                              // row in the 16-row block
+    const uint32_t lchunk = static_cast<uint32_t>((lane & 3) ^ ((lane >> 3) & 3));      // swizzled 16-byte chunk
+    uint32_t voff[C::MAXL];
 #pragma unroll
-    for (int q = 0; q < C::A_LOADS; ++q)
-        a_voff[q] = static_cast<uint32_t>((q * 4 + wave) * 8 + (lane >> 3)) * lda2 + swz_chunk * 16u;
-#pragma unroll
-    for (int q = 0; q < C::B_LOADS; ++q)
-        b_voff[q] = static_cast<uint32_t>((q * 4 + wave) * 8 + (lane >> 3)) * ldb2 + swz_chunk * 16u;
-    uint32_t frag_off[2];   // row (lane & 15), logical chunk kk*4 + (lane >> 4), swizzled by row & 7
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-        frag_off[kk] = static_cast<uint32_t>((lane & 15) * 128 + ((((kk * 4) + (lane >> 4)) ^ (lane & 7)) << 4));
+    for (int j = 0; j < C::MAXL; ++j) {
+        const int i = wave + 4 * j;
+        voff[j] = (j < C::A_J) ? (static_cast<uint32_t>(i * 16) + lrow) * lda2 + lchunk * 16u
+                               : (static_cast<uint32_t>((i - C::A_INSTR) * 16) + lrow) * ldb2 + lchunk * 16u;
+    }
+    // fragment: row (lane & 15) of a 16-row block, logical chunk (lane >> 4), swizzled by (row >> 1) & 3
+    const uint32_t frag_off = static_cast<uint32_t>((lane & 15) * C::ROW_BYTES +
+                                                    (((lane >> 4) ^ (((lane & 15) >> 1) & 3)) << 4));
+    const uint32_t a_frag = static_cast<uint32_t>(wm * C::WTM * C::ROW_BYTES) + frag_off;
+    const uint32_t b_frag = static_cast<uint32_t>(C::A_BYTES + wn * C::WTN * C::ROW_BYTES) + frag_off;
 
-    const int kt_total = a.K / 64;
+    const int kt_total = a.K / 32;
     const uint32_t out_row_bytes = static_cast<uint32_t>(a.N) * 2u;
     const int nprog = gridDim.x;
     const int p = blockIdx.x;
@@ -216,53 +252,78 @@ __global__ __launch_bounds__(256) void ag_gemm_kernel(GemmKernelArgs a)
         for (int bm = 0; bm < C::BM; ++bm)
 #pragma unroll
             for (int bn = 0; bn < C::BN; ++bn) acc[bm][bn] = f32x4{0.f, 0.f, 0.f, 0.f};
+        V fa[2][C::BM], fb[2][C::BN];
 
-        auto compute = [&](const uint8_t* buf) {
-            const uint8_t* abuf = buf + wm * C::WTM * 128;
-            const uint8_t* bbuf = buf + C::A_BYTES + wn * C::WTN * 128;
+        auto issue = [&](uint8_t* slot, int kt) {
+            const bool live = kt < kt_total;
+            Stage<C>::load(a_base, live ? a_records : 0, b_base, live ? b_records : 0, slot, kt, wave, voff);
+        };
+        // Fragment reads are issued as inline assembly: the compiler cannot
+        // tell these LDS reads apart from the LDS-direct loads still landing in
+        // other ring slots and would otherwise wait for all of them.  Their
+        // completion is awaited explicitly (lgkmcnt) before the data is used.
+        auto read_frags = [&](const uint8_t* slot, int f) {
+            const uint32_t sa = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const AG_LDS uint8_t*)slot)) + a_frag;
+            const uint32_t sb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const AG_LDS uint8_t*)slot)) + b_frag;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                V af[C::BM], bf[C::BN];
+            for (int bm = 0; bm < C::BM; ++bm) Frag<C>::read(fa[f][bm], sa, bm);
 #pragma unroll
-                for (int bm = 0; bm < C::BM; ++bm)
-                    af[bm] = *reinterpret_cast<const V*>(abuf + bm * 16 * 128 + frag_off[kk]);
+            for (int bn = 0; bn < C::BN; ++bn) Frag<C>::read(fb[f][bn], sb, bn);
+        };
+        auto mfmas = [&](int f) {
 #pragma unroll
-                for (int bn = 0; bn < C::BN; ++bn)
-                    bf[bn] = *reinterpret_cast<const V*>(bbuf + bn * 16 * 128 + frag_off[kk]);
+            for (int bm = 0; bm < C::BM; ++bm)
 #pragma unroll
-                for (int bm = 0; bm < C::BM; ++bm)
-#pragma unroll
-                    for (int bn = 0; bn < C::BN; ++bn) acc[bm][bn] = M::run(bf[bn], af[bm], acc[bm][bn]);
-            }
+                for (int bn = 0; bn < C::BN; ++bn) acc[bm][bn] = M::run(fb[f][bn], fa[f][bm], acc[bm][bn]);
+        };
+        auto wait_two_stages = [&]() {   // every load of this wave but the last two stages' has landed
+            if (full_share) wait_vmcnt<2 * C::MAXL>();
+            else wait_vmcnt<2 * (C::MAXL - 1)>();
+        };
+        // step s: stage s+1 is made visible, stage s+4 starts loading into the
+        // slot stage s occupied, fragments of stage s+1 are read while the
+        // MFMAs of stage s run
+        auto step = [&](int s, uint8_t* cur, uint8_t* next, int f) {
+            __builtin_amdgcn_sched_barrier(0);
+            wait_two_stages();
+            wait_lgkmcnt0();              // this wave's fragment reads of stage s are complete
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            issue(cur, s + 4);
+            if (s + 1 < kt_total) read_frags(next, f ^ 1);
+            mfmas(f);
         };
 
-        // ---- K loop: two LDS stages used in turn
-        Stage<C>::load(a_base, a_records, b_base, b_records, lds0, 0, wave, a_voff, b_voff);
-        int kt = 0;
-        for (; kt + 2 <= kt_total; kt += 2) {
-            wait_vmcnt<0>();
-            __builtin_amdgcn_s_barrier();
-            Stage<C>::load(a_base, a_records, b_base, b_records, lds1, kt + 1, wave, a_voff, b_voff);
-            compute(lds0);
-            wait_vmcnt<0>();
-            __builtin_amdgcn_s_barrier();
-            if (kt + 2 < kt_total) Stage<C>::load(a_base, a_records, b_base, b_records, lds0, kt + 2, wave, a_voff, b_voff);
-            compute(lds1);
-        }
-        if (kt < kt_total) {   // odd number of K steps
-            wait_vmcnt<0>();
-            __builtin_amdgcn_s_barrier();
-            compute(lds0);
+        // ---- prologue: stages 0..3 in flight, stage 0's fragments in registers
+        issue(ring0, 0);
+        issue(ring1, 1);
+        issue(ring2, 2);
+        issue(ring3, 3);
+        if (full_share) wait_vmcnt<3 * C::MAXL>();
+        else wait_vmcnt<3 * (C::MAXL - 1)>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(ring0, 0);
+
+        // ---- K loop, unrolled over the four slots
+        for (int s = 0; s < kt_total; s += 4) {
+            step(s, ring0, ring1, 0);
+            if (s + 1 < kt_total) step(s + 1, ring1, ring2, 1);
+            if (s + 2 < kt_total) step(s + 2, ring2, ring3, 0);
+            if (s + 3 < kt_total) step(s + 3, ring3, ring0, 1);
         }
 
-        // ---- epilogue: round, stage C through LDS, store to every destination
+        // ---- epilogue: round, stage C through the ring, store to every destination
+        wait_vmcnt<0>();                // loads of stages past the end have landed too
         wait_lgkmcnt0();
-        __builtin_amdgcn_s_barrier();   // every wave is done reading the stages
+        __builtin_amdgcn_s_barrier();
         {
-            uint8_t* half = wm == 0 ? lds0 : lds1;   // wave rows lie in one half of the tile
 #pragma unroll
             for (int bm = 0; bm < C::BM; ++bm) {
-                const int row = bm * 16 + (lane & 15);
+                const int trow = wm * C::WTM + bm * 16;          // first tile row of this block row
+                const int q = trow / C::QROWS;                   // ring slot holding these rows
+                uint8_t* slot = q == 0 ? ring0 : q == 1 ? ring1 : q == 2 ? ring2 : ring3;
+                const int row = trow - q * C::QROWS + (lane & 15);
 #pragma unroll
                 for (int bn = 0; bn < C::BN; ++bn) {
                     const int byte_col = (wn * C::WTN + bn * 16) * 2 + (lane >> 4) * 8;
@@ -272,29 +333,34 @@ __global__ __launch_bounds__(256) void ag_gemm_kernel(GemmKernelArgs a)
                     u32x2 packed;
                     packed.x = M::pack(c[0], c[1]);
                     packed.y = M::pack(c[2], c[3]);
-                    *reinterpret_cast<u32x2*>(half + row * C::C_PITCH + chunk * 16 + (byte_col & 15)) = packed;
+                    *reinterpret_cast<u32x2*>(slot + row * C::C_PITCH + chunk * 16 + (byte_col & 15)) = packed;
                 }
             }
         }
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
         {
+            // opaque copy of the thread index: keeps the epilogue's lane
+            // arithmetic here instead of live (and spilled) across the K loop
+            int etid = tid;
+            asm volatile("" : "+v"(etid));
             const uint64_t tile_off = (static_cast<uint64_t>(m0) * a.N + n0) * 2u;
             const uint64_t records = static_cast<uint64_t>(a.M - m0) * out_row_bytes - static_cast<uint64_t>(n0) * 2u;
             const int cols_left = a.N - n0;
             u32x4 vals[C::CHUNKS_PER_THREAD];
-            uint32_t voff[C::CHUNKS_PER_THREAD];
+            uint32_t ooff[C::CHUNKS_PER_THREAD];
 #pragma unroll
             for (int j = 0; j < C::CHUNKS_PER_THREAD; ++j) {
-                const int ci = tid + 256 * j;
+                const int ci = etid + 256 * j;
                 const int row = ci / C::CPR;
                 const int c = ci - row * C::CPR;
-                constexpr int kHalfChunks = C::HALF_ROWS * C::CPR;
-                const uint8_t* half = (256 * j < kHalfChunks) ? lds0 : lds1;
-                const int hrow = (256 * j < kHalfChunks) ? row : row - C::HALF_ROWS;
-                const int pc = C::XOR_SWIZZLE ? (c ^ (hrow & 15)) : c;
-                vals[j] = *reinterpret_cast<const u32x4*>(half + hrow * C::C_PITCH + pc * 16);
-                voff[j] = (c * 8 < cols_left) ? static_cast<uint32_t>(row) * out_row_bytes + static_cast<uint32_t>(c) * 16u
+                constexpr int kSlotChunks = C::QROWS * C::CPR;
+                const int q = (256 * j) / kSlotChunks;           // uniform: slots hold whole rounds
+                const uint8_t* slot = q == 0 ? ring0 : q == 1 ? ring1 : q == 2 ? ring2 : ring3;
+                const int qrow = row - q * C::QROWS;
+                const int pc = C::XOR_SWIZZLE ? (c ^ (qrow & 15)) : c;
+                vals[j] = *reinterpret_cast<const u32x4*>(slot + qrow * C::C_PITCH + pc * 16);
+                ooff[j] = (c * 8 < cols_left) ? static_cast<uint32_t>(row) * out_row_bytes + static_cast<uint32_t>(c) * 16u
                                               : kOutOfRange;
             }
 #pragma unroll
@@ -302,7 +368,7 @@ __global__ __launch_bounds__(256) void ag_gemm_kernel(GemmKernelArgs a)
                 const __amdgpu_buffer_rsrc_t rd = make_rsrc(dest[i] + tile_off, records);
 #pragma unroll
                 for (int j = 0; j < C::CHUNKS_PER_THREAD; ++j)
-                    __builtin_amdgcn_raw_buffer_store_b128(vals[j], rd, voff[j], 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(vals[j], rd, ooff[j], 0, 0);
             }
         }
         wait_lgkmcnt0();

@@ -1,0 +1,162 @@
+"""Code-generation checks on our own gfx950 assembly (compile only, no GPU).
+
+The pages judge the hoisting by the generated code (ROCm/iris #626,
+"Assembly" table; ROCm/iris #594, "Compiler inspection and grouping"):
+heap-base loads precede the tile loop, the only load inside it is the input
+tile, no destination store is preceded by a full drain, the destination
+loop has no back-edge, and VGPR/SGPR/spill counts are reported.  These tests
+compile the kernels with hipcc for gfx950 and check the same properties.
+"""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "gemm_all_gather_amd", "csrc")
+
+pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                                reason="hipcc not available")
+
+
+def _hipcc():
+    return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = {}
+    d = tmp_path_factory.mktemp("isa")
+    for src in ("ag_copy.hip", "ag_gemm.hip"):
+        s = str(d / (src + ".s"))
+        cmd = [_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops", f"-I{CSRC}", f"-I{os.path.join(ROOT, 'include')}", "--cuda-device-only", "-S",
+               "-o", s, os.path.join(CSRC, src)]
+        subprocess.run(cmd, check=True, capture_output=True)
+        out[src] = open(s).read()
+    return out
+
+
+def _kernel_body(text, pattern):
+    """Instructions of the first kernel whose symbol matches pattern (comments dropped)."""
+    m = re.search(r"^(_Z\S*" + pattern + r"\S*):", text, re.M)
+    assert m, pattern
+    start = m.end()
+    end = text.index("s_endpgm", start)
+    lines = []
+    for ln in text[start:end].splitlines():
+        ln = ln.split(";", 1)[0].rstrip()
+        if ln.strip():
+            lines.append(ln.strip())
+    return m.group(1), lines
+
+
+def _meta(text, symbol):
+    m = re.search(r"\.amdhsa_kernel " + re.escape(symbol) + r"\n(.*?)\.end_amdhsa_kernel", text, re.S)
+    body = m.group(1)
+    g = lambda k: int(re.search(r"\." + k + r" (\d+)", body).group(1))
+    return {"vgpr": g("amdhsa_next_free_vgpr"), "sgpr": g("amdhsa_next_free_sgpr"),
+            "scratch": g("amdhsa_private_segment_fixed_size"), "lds": g("amdhsa_group_segment_fixed_size"),
+            "agpr_offset": g("amdhsa_accum_offset")}
+
+
+def _loops(lines):
+    """(header_index, backedge_index) of every loop: a branch to a label defined earlier."""
+    labels = {ln[:-1]: i for i, ln in enumerate(lines) if ln.endswith(":")}
+    out = []
+    for i, ln in enumerate(lines):
+        m = re.match(r"s_(?:cbranch_\w+|branch)\s+(\S+)", ln)
+        if m and m.group(1) in labels and labels[m.group(1)] < i:
+            out.append((labels[m.group(1)], i))
+    return out
+
+
+def _outermost(loops):
+    return max(loops, key=lambda x: x[1] - x[0])
+
+
+COPY_CASES = [("16", "8", "1"), ("16", "8", "2"), ("8", "8", "2"), ("16", "4", "1"), ("4", "2", "4")]
+
+
+@pytest.mark.parametrize("vec,w,vpt", COPY_CASES)
+def test_copy_kernel_hoists_bases_and_never_drains_before_a_store(asm, vec, w, vpt):
+    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_copy_kernelILi{vec}ELi{w}ELi{vpt}E")
+    W, VPT = int(w), int(vpt)
+    loops = _loops(lines)
+    assert loops, "tile loop not found"
+    h, b = _outermost(loops)
+    body = lines[h:b + 1]
+    prologue = lines[:h]
+    # every heap-base (scalar) load happens before the tile loop
+    assert not any(ln.startswith("s_load") for ln in body), "scalar load inside the tile loop"
+    assert sum(ln.startswith("s_load_dwordx2") for ln in prologue) >= W
+    # the only loads in the loop are the input tile's (two tiles per unrolled loop trip)
+    loads = [ln for ln in body if re.match(r"(buffer|global|flat)_load", ln)]
+    assert len(loads) == 2 * VPT, loads
+    stores = [i for i, ln in enumerate(body) if ln.startswith("buffer_store")]
+    assert len(stores) == 2 * W * VPT
+    # no store is preceded (since the previous store) by a wait that drains the memory counter
+    prev = 0
+    for i in stores:
+        waits = [ln for ln in body[prev:i] if ln.startswith("s_waitcnt") and "vmcnt(0)" in ln]
+        assert not waits, f"drain before a store: {waits}"
+        prev = i
+    # the destination stores of one tile are straight-line code: no branch between them
+    for first, last in ((stores[0], stores[W * VPT - 1]), (stores[W * VPT], stores[-1])):
+        assert not any(re.match(r"s_(cbranch|branch)", ln) for ln in body[first:last]), "destination loop back-edge"
+    meta = _meta(asm["ag_copy.hip"], sym)
+    assert meta["scratch"] == 0, meta
+
+
+@pytest.mark.parametrize("cfg", ["256ELi224", "256ELi256", "128ELi128"])
+@pytest.mark.parametrize("dt", ["Lb0", "Lb1"])
+def test_gemm_kernel_structure(asm, cfg, dt):
+    sym, lines = _kernel_body(asm["ag_gemm.hip"], f"ag_gemm_kernelI{dt}ELi8ENS_8gemm_cfg3CfgILi{cfg}EEEE")
+    first_barrier = next(i for i, ln in enumerate(lines) if ln.startswith("s_barrier"))
+    # heap-base loads: all W of them before any tile or K-loop code (block layout may reorder the rest)
+    assert sum(ln.startswith("s_load_dwordx2") for ln in lines[:first_barrier]) >= 8
+    assert not any(ln.startswith("s_load_dwordx2") for ln in lines[first_barrier:])
+    # K loop: runs of back-to-back MFMAs with no memory waits, spills or stores inside, and no
+    # drain of the memory counter right before a run
+    runs, i = [], 0
+    while i < len(lines):
+        if lines[i].startswith("v_mfma"):
+            j = i
+            while j < len(lines) and not lines[j].endswith(":") and not re.match(r"s_(cbranch|branch|barrier)", lines[j]):
+                j += 1
+            runs.append((i, j))
+            i = j
+        i += 1
+    mfma = [ln for ln in lines if ln.startswith("v_mfma")]
+    assert mfma and all(ln.startswith("v_mfma_f32_16x16x32_" + ("bf16" if dt == "Lb1" else "f16")) for ln in mfma)
+    big = [(a, b) for a, b in runs if sum(lines[k].startswith("v_mfma") for k in range(a, b)) >= 16]
+    assert big, "no MFMA run found"
+    for a, b in big:
+        seg = lines[a:b]
+        assert not any(ln.startswith(("scratch_", "buffer_store", "s_waitcnt")) for ln in seg), seg[:5]
+        assert not any(ln.startswith("s_waitcnt") and "vmcnt(0)" in ln for ln in lines[max(0, a - 40):a])
+    assert any(re.match(r"buffer_load_dwordx4 .* lds", ln) for ln in lines)
+    # epilogue: the W destination stores of a tile form one straight run with no drain inside
+    stores = [i for i, ln in enumerate(lines) if ln.startswith("buffer_store_dwordx4")]
+    assert stores
+    seg = lines[stores[0]:stores[-1]]
+    assert not any(ln.startswith("s_waitcnt") and "vmcnt(0)" in ln for ln in seg)
+    assert not any(re.match(r"s_(cbranch|branch)", ln) for ln in seg)
+
+
+def test_report_registers(asm, capsys):
+    """Print VGPR/AGPR/SGPR/scratch/LDS per instantiation (reported next to timings)."""
+    rows = []
+    for src, pat in (("ag_copy.hip", r"ag_copy_kernel\S+"), ("ag_gemm.hip", r"ag_gemm_kernel\S+")):
+        for sym in re.findall(r"^\s*\.amdhsa_kernel (\S+)\s*$", asm[src], re.M):
+            if re.search(pat, sym):
+                rows.append((sym, _meta(asm[src], sym)))
+    assert rows
+    with capsys.disabled():
+        for sym, m in rows[:6] + rows[-6:]:
+            print(f"{sym[:80]:80s} {m}")
+    # the copy kernels never spill
+    assert all(m["scratch"] == 0 for s, m in rows if "ag_copy_kernel" in s)
