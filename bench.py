@@ -192,38 +192,38 @@ def main() -> int:
         fused_ok = False
         fused_reason = str(exc)
 
-    # ---------------- warm-up and timed region
-    for _ in range(args.warmup):
-        copy_job()
-        if fused_ok:
-            fused_job()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        copy_job()
-        ev[k][1].record(stream)
-        if fused_ok:
-            fused_job()
-        ev[k][2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    # ---------------- warm-up and timed regions: the all-gather job K times, then the fused job K
+    # times, each region bracketed by device synchronisation; a step is one of each
+    def timed(job):
+        for _ in range(args.warmup):
+            job()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            ev[k][0].record(stream)
+            job()
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return sum(a.elapsed_time(b) for a, b in ev) / args.steps, wall
+
+    copy_ms, wall_copy = timed(copy_job) if args.only != "fused" else (0.0, 0.0)
+    fused_ms, wall_fused = timed(fused_job) if (fused_ok and args.only != "copy") else (0.0, 0.0)
+    step_ms = copy_ms + fused_ms
+    wall = wall_copy + wall_fused
     if args.calib_copy_mib > 0:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    copy_ms = sum(ev[k][0].elapsed_time(ev[k][1]) for k in range(args.steps)) / args.steps
-    fused_ms = sum(ev[k][1].elapsed_time(ev[k][2]) for k in range(args.steps)) / args.steps
-    step_ms = sum(ev[k][0].elapsed_time(ev[k][2]) for k in range(args.steps)) / args.steps
 
     # ---------------- rates and rooflines
     per_call_bytes = ag_plan.bytes_read + ag_plan.bytes_written          # (1+W) * M_local * N * e
-    copy_launch_s = copy_ms / 1e3 / AG_W
-    copy_gbs = AG_W * per_call_bytes / (copy_ms / 1e3) / 1e9
+    copy_launch_s = max(copy_ms, 1e-9) / 1e3 / AG_W     # profiling runs with --only fused time no copy
+    copy_gbs = AG_W * per_call_bytes / (max(copy_ms, 1e-9) / 1e3) / 1e9
     traffic = _traffic("ag_copy_kernel_w8_1024x4096_f16_pmc.md", "ag_copy.hip", per_call_bytes)
     out = {
         "metric": METRIC,
@@ -263,8 +263,8 @@ def main() -> int:
     }
     if fused_ok:
         flops = fu_plan.flops
-        fu_launch_s = fused_ms / 1e3 / FU_W
-        fu_tflops = FU_W * flops / (fused_ms / 1e3) / 1e12
+        fu_launch_s = max(fused_ms, 1e-9) / 1e3 / FU_W
+        fu_tflops = FU_W * flops / (max(fused_ms, 1e-9) / 1e3) / 1e12
         out["fused"] = {
             "metric": "fused GEMM+all-gather TFLOP/s",
             "value": round(fu_tflops, 2),

@@ -46,6 +46,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kRawBufferWord3 = 0x00020000;
+// Cache-policy bits of the epilogue stores (bit 1 = non-temporal).
+#ifndef AG_GEMM_STORE_AUX
+#define AG_GEMM_STORE_AUX 2
+#endif
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(uint64_t base, uint64_t records)
@@ -97,7 +101,7 @@ struct Cfg {
     static constexpr int WGM = 2, WGN = 2;                 // wave grid
     static constexpr int WTM = TM / WGM, WTN = TN / WGN;   // wave sub-tile
     static constexpr int BM = WTM / 16, BN = WTN / 16;     // 16x16 blocks per wave
-    static constexpr int NS = 4;                           // LDS ring slots
+    static constexpr int NS = 5;                           // LDS ring slots
     static constexpr int ROW_BYTES = 64;                   // one stage: K = 32 values of 2 bytes per row
     static constexpr int A_BYTES = TM * ROW_BYTES;
     static constexpr int STAGE = (TM + TN) * ROW_BYTES;
@@ -175,12 +179,12 @@ __global__ __launch_bounds__(256) void ag_gemm_kernel(GemmKernelArgs a)
 {
     using M = Mfma<BF16>;
     using V = typename M::V;
-    // four ring slots as separate objects, so the compiler can tell a read of
-    // one slot from an LDS-direct load still landing in another
+    // five ring slots as separate objects
     __shared__ __attribute__((aligned(1024))) uint8_t ring0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t ring1[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t ring2[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t ring3[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring4[C::STAGE];
 
     // ---- destinations, translated once above the tile and K loops
     uint64_t base[W];
@@ -276,20 +280,21 @@ __global__ __launch_bounds__(256) void ag_gemm_kernel(GemmKernelArgs a)
 #pragma unroll
                 for (int bn = 0; bn < C::BN; ++bn) acc[bm][bn] = M::run(fb[f][bn], fa[f][bm], acc[bm][bn]);
         };
-        auto wait_two_stages = [&]() {   // every load of this wave but the last two stages' has landed
-            if (full_share) wait_vmcnt<2 * C::MAXL>();
-            else wait_vmcnt<2 * (C::MAXL - 1)>();
+        auto wait_three_stages = [&]() {   // every load of this wave but the last three stages' has landed
+            if (full_share) wait_vmcnt<3 * C::MAXL>();
+            else wait_vmcnt<3 * (C::MAXL - 1)>();
         };
-        // step s: stage s+1 is made visible, stage s+4 starts loading into the
-        // slot stage s occupied, fragments of stage s+1 are read while the
-        // MFMAs of stage s run
-        auto step = [&](int s, uint8_t* cur, uint8_t* next, int f) {
+        // step s: stage s+4 starts loading into the slot of stage s-1 (whose
+        // fragments every wave read before the previous barrier), stage s+1 is
+        // made visible, its fragments are read while the MFMAs of stage s run.
+        // Four stages are in flight while a stage is computed.
+        auto step = [&](int s, uint8_t* refill, uint8_t* next, int f) {
             __builtin_amdgcn_sched_barrier(0);
-            wait_two_stages();
+            issue(refill, s + 4);
+            wait_three_stages();
             wait_lgkmcnt0();              // this wave's fragment reads of stage s are complete
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            issue(cur, s + 4);
             if (s + 1 < kt_total) read_frags(next, f ^ 1);
             mfmas(f);
         };
@@ -299,18 +304,23 @@ __global__ __launch_bounds__(256) void ag_gemm_kernel(GemmKernelArgs a)
         issue(ring1, 1);
         issue(ring2, 2);
         issue(ring3, 3);
-        if (full_share) wait_vmcnt<3 * C::MAXL>();
-        else wait_vmcnt<3 * (C::MAXL - 1)>();
+        wait_three_stages();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         read_frags(ring0, 0);
 
-        // ---- K loop, unrolled over the four slots
-        for (int s = 0; s < kt_total; s += 4) {
-            step(s, ring0, ring1, 0);
-            if (s + 1 < kt_total) step(s + 1, ring1, ring2, 1);
-            if (s + 2 < kt_total) step(s + 2, ring2, ring3, 0);
-            if (s + 3 < kt_total) step(s + 3, ring3, ring0, 1);
+        // ---- K loop, unrolled over the five slots and the two fragment buffers
+        for (int s = 0; s < kt_total; s += 10) {
+            step(s, ring4, ring1, 0);
+            if (s + 1 < kt_total) step(s + 1, ring0, ring2, 1);
+            if (s + 2 < kt_total) step(s + 2, ring1, ring3, 0);
+            if (s + 3 < kt_total) step(s + 3, ring2, ring4, 1);
+            if (s + 4 < kt_total) step(s + 4, ring3, ring0, 0);
+            if (s + 5 < kt_total) step(s + 5, ring4, ring1, 1);
+            if (s + 6 < kt_total) step(s + 6, ring0, ring2, 0);
+            if (s + 7 < kt_total) step(s + 7, ring1, ring3, 1);
+            if (s + 8 < kt_total) step(s + 8, ring2, ring4, 0);
+            if (s + 9 < kt_total) step(s + 9, ring3, ring0, 1);
         }
 
         // ---- epilogue: round, stage C through the ring, store to every destination
@@ -368,7 +378,7 @@ __global__ __launch_bounds__(256) void ag_gemm_kernel(GemmKernelArgs a)
                 const __amdgpu_buffer_rsrc_t rd = make_rsrc(dest[i] + tile_off, records);
 #pragma unroll
                 for (int j = 0; j < C::CHUNKS_PER_THREAD; ++j)
-                    __builtin_amdgcn_raw_buffer_store_b128(vals[j], rd, ooff[j], 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(vals[j], rd, ooff[j], 0, AG_GEMM_STORE_AUX);
             }
         }
         wait_lgkmcnt0();
