@@ -46,6 +46,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kRawBufferWord3 = 0x00020000;
+// Wave rows of the 2-column wave grid (4: eight waves, two per SIMD).
+#ifndef AG_GEMM_WGM
+#define AG_GEMM_WGM 4
+#endif
 // Cache-policy bits of the epilogue stores (bit 1 = non-temporal).
 #ifndef AG_GEMM_STORE_AUX
 #define AG_GEMM_STORE_AUX 2
@@ -95,10 +99,12 @@ template <> struct Mfma<true> {
 // Tile configuration.  Named namespace: a kernel template instantiated with a
 // type of internal linkage gets no host-side launch handle.
 namespace gemm_cfg {
-template <int TM_, int TN_>
+template <int TM_, int TN_, int WGM_, int WGN_>
 struct Cfg {
     static constexpr int TM = TM_, TN = TN_;
-    static constexpr int WGM = 2, WGN = 2;                 // wave grid
+    static constexpr int WGM = WGM_, WGN = WGN_;           // wave grid
+    static constexpr int NW = WGM * WGN;                   // waves per workgroup
+    static constexpr int NT = 64 * NW;                     // threads per workgroup
     static constexpr int WTM = TM / WGM, WTN = TN / WGN;   // wave sub-tile
     static constexpr int BM = WTM / 16, BN = WTN / 16;     // 16x16 blocks per wave
     static constexpr int NS = 5;                           // LDS ring slots
@@ -108,18 +114,19 @@ struct Cfg {
     static constexpr int A_INSTR = TM / 16;                // 1-KiB wave loads (16 rows) per stage
     static constexpr int B_INSTR = TN / 16;
     static constexpr int INSTR = A_INSTR + B_INSTR;
-    static constexpr int A_J = A_INSTR / 4;                // loads j < A_J of every wave are A rows
-    static constexpr int MAXL = (INSTR + 3) / 4;           // loads per wave per stage (waves 0..)
+    static constexpr int A_J = A_INSTR / NW;               // loads j < A_J of every wave are A rows
+    static constexpr int MAXL = (INSTR + NW - 1) / NW;     // loads per wave per stage (waves 0..)
     static constexpr int CPR = TN / 8;                     // 16-byte chunks per C row
     static constexpr bool XOR_SWIZZLE = (CPR & (CPR - 1)) == 0 && CPR >= 16;
     static constexpr int C_PITCH = XOR_SWIZZLE ? TN * 2 : TN * 2 + 16;
-    static constexpr int QROWS = TM / 4;                   // C rows staged in each ring slot
-    static constexpr int CHUNKS_PER_THREAD = TM * CPR / 256;
+    static constexpr int QROWS = TM / 4;                   // C rows staged in each of four ring slots
+    static constexpr int SLOT_CHUNKS = QROWS * CPR;        // 16-byte C chunks per staging slot
+    static constexpr int ROUNDS = (SLOT_CHUNKS + NT - 1) / NT;   // chunk rounds per slot per thread
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be made of 16x16 blocks");
     static_assert(TM % 64 == 0 && TN % 16 == 0, "stage loads move 16 rows per wave instruction");
     static_assert(QROWS * C_PITCH <= STAGE, "a quarter of the C tile must fit in one ring slot");
-    static_assert((QROWS * CPR) % 256 == 0, "each ring slot must hold whole rounds of C chunks");
-    static_assert(WTM % QROWS == 0 || QROWS % 16 == 0, "wave rows map to whole ring slots per block row");
+    static_assert(QROWS % 16 == 0, "a 16-row accumulator block never straddles two staging slots");
+    static_assert(A_INSTR % NW == 0, "every wave issues the same number of A loads");
     static_assert(NS * STAGE <= 160 * 1024, "gfx950 has 160 KiB of LDS");
 };
 }  // namespace gemm_cfg
@@ -130,7 +137,7 @@ using gemm_cfg::Cfg;
 // One K stage (32 wide) of the A and B tiles, global -> LDS.  Wave
 // instruction i of the stage moves 16 rows x 64 bytes (A rows for
 // i < A_INSTR, then B rows) to LDS bytes [i*1024, i*1024 + 1024) of the
-// slot; wave w issues instructions w, w+4, ...  A descriptor of size 0 turns
+// slot; wave w issues instructions w, w+NW, ...  A descriptor of size 0 turns
 // the loads of a stage past the end of K into no-ops that still count.
 // (Descriptors are passed as base + size: a template whose signature names
 // the buffer-resource type fails to substitute in the host compilation pass.)
@@ -164,7 +171,7 @@ struct Stage {
         const uint32_t soff = static_cast<uint32_t>(kt) * 64u;   // k0 * 2 bytes
 #pragma unroll
         for (int j = 0; j < C::MAXL; ++j) {
-            const int i = wave + 4 * j;
+            const int i = wave + C::NW * j;
             if (j < C::A_J) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (AG_LDS void*)(slot + i * 1024), 16, voff[j], soff, 0, 0);
             } else if (i < C::INSTR) {
@@ -175,7 +182,7 @@ struct Stage {
 };
 
 template <bool BF16, int W, class C>
-__global__ __launch_bounds__(256) void ag_gemm_kernel(GemmKernelArgs a)
+__global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
 {
     using M = Mfma<BF16>;
     using V = typename M::V;
@@ -206,7 +213,7 @@ __global__ __launch_bounds__(256) void ag_gemm_kernel(GemmKernelArgs a)
     const int wm = wave / C::WGN;
     const int wn = wave % C::WGN;
     // loads per stage of this wave (MAXL or MAXL-1)
-    const bool full_share = wave + 4 * (C::MAXL - 1) < C::INSTR;
+    const bool full_share = wave + C::NW * (C::MAXL - 1) < C::INSTR;
 
     // ---- tile-invariant lane offsets
     const uint32_t lda2 = static_cast<uint32_t>(a.lda) * 2u;
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(256) void ag_gemm_kernel(GemmKernelArgs a)
     uint32_t voff[C::MAXL];
 #pragma unroll
     for (int j = 0; j < C::MAXL; ++j) {
-        const int i = wave + 4 * j;
+        const int i = wave + C::NW * j;
         voff[j] = (j < C::A_J) ? (static_cast<uint32_t>(i * 16) + lrow) * lda2 + lchunk * 16u
                                : (static_cast<uint32_t>((i - C::A_INSTR) * 16) + lrow) * ldb2 + lchunk * 16u;
     }
@@ -357,27 +364,32 @@ __global__ __launch_bounds__(256) void ag_gemm_kernel(GemmKernelArgs a)
             const uint64_t tile_off = (static_cast<uint64_t>(m0) * a.N + n0) * 2u;
             const uint64_t records = static_cast<uint64_t>(a.M - m0) * out_row_bytes - static_cast<uint64_t>(n0) * 2u;
             const int cols_left = a.N - n0;
-            u32x4 vals[C::CHUNKS_PER_THREAD];
-            uint32_t ooff[C::CHUNKS_PER_THREAD];
+            constexpr int NCH = 4 * C::ROUNDS;
+            u32x4 vals[NCH];
+            uint32_t ooff[NCH];
 #pragma unroll
-            for (int j = 0; j < C::CHUNKS_PER_THREAD; ++j) {
-                const int ci = etid + 256 * j;
-                const int row = ci / C::CPR;
-                const int c = ci - row * C::CPR;
-                constexpr int kSlotChunks = C::QROWS * C::CPR;
-                const int q = (256 * j) / kSlotChunks;           // uniform: slots hold whole rounds
+            for (int q = 0; q < 4; ++q) {
                 const uint8_t* slot = q == 0 ? ring0 : q == 1 ? ring1 : q == 2 ? ring2 : ring3;
-                const int qrow = row - q * C::QROWS;
-                const int pc = C::XOR_SWIZZLE ? (c ^ (qrow & 15)) : c;
-                vals[j] = *reinterpret_cast<const u32x4*>(slot + qrow * C::C_PITCH + pc * 16);
-                ooff[j] = (c * 8 < cols_left) ? static_cast<uint32_t>(row) * out_row_bytes + static_cast<uint32_t>(c) * 16u
-                                              : kOutOfRange;
+#pragma unroll
+                for (int rr = 0; rr < C::ROUNDS; ++rr) {
+                    const int ci = etid + C::NT * rr;             // chunk within this slot
+                    const bool live = (C::SLOT_CHUNKS % C::NT == 0) || ci < C::SLOT_CHUNKS;
+                    const int cic = live ? ci : 0;
+                    const int qrow = cic / C::CPR;
+                    const int c = cic - qrow * C::CPR;
+                    const int row = q * C::QROWS + qrow;
+                    const int pc = C::XOR_SWIZZLE ? (c ^ (qrow & 15)) : c;
+                    vals[q * C::ROUNDS + rr] = *reinterpret_cast<const u32x4*>(slot + qrow * C::C_PITCH + pc * 16);
+                    ooff[q * C::ROUNDS + rr] = (live && c * 8 < cols_left)
+                                                   ? static_cast<uint32_t>(row) * out_row_bytes + static_cast<uint32_t>(c) * 16u
+                                                   : kOutOfRange;
+                }
             }
 #pragma unroll
             for (int i = 0; i < W; ++i) {   // local region first, then the rotated peers
                 const __amdgpu_buffer_rsrc_t rd = make_rsrc(dest[i] + tile_off, records);
 #pragma unroll
-                for (int j = 0; j < C::CHUNKS_PER_THREAD; ++j)
+                for (int j = 0; j < NCH; ++j)
                     __builtin_amdgcn_raw_buffer_store_b128(vals[j], rd, ooff[j], 0, AG_GEMM_STORE_AUX);
             }
         }
@@ -408,9 +420,9 @@ template <bool BF16>
 GemmFn pick_cfg(int cfg, int w)
 {
     switch (cfg) {
-    case kGemmTile256x256: return pick_world<BF16, Cfg<256, 256>>(w);
-    case kGemmTile256x224: return pick_world<BF16, Cfg<256, 224>>(w);
-    case kGemmTile128x128: return pick_world<BF16, Cfg<128, 128>>(w);
+    case kGemmTile256x256: return pick_world<BF16, Cfg<256, 256, AG_GEMM_WGM, 2>>(w);
+    case kGemmTile256x224: return pick_world<BF16, Cfg<256, 224, AG_GEMM_WGM, 2>>(w);
+    case kGemmTile128x128: return pick_world<BF16, Cfg<128, 128, AG_GEMM_WGM, 2>>(w);
     default: return nullptr;
     }
 }
@@ -421,7 +433,7 @@ hipError_t launch_gemm(const GemmLaunch& l, hipStream_t stream)
 {
     GemmFn fn = l.bf16 ? pick_cfg<true>(l.cfg, l.world) : pick_cfg<false>(l.cfg, l.world);
     if (fn == nullptr || l.grid < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(l.grid), dim3(256), 0, stream, l.args);
+    hipLaunchKernelGGL(fn, dim3(l.grid), dim3(64 * AG_GEMM_WGM * 2), 0, stream, l.args);
     return hipGetLastError();
 }
 

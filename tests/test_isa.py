@@ -114,7 +114,7 @@ def test_copy_kernel_hoists_bases_and_never_drains_before_a_store(asm, vec, w, v
 @pytest.mark.parametrize("cfg", ["256ELi224", "256ELi256", "128ELi128"])
 @pytest.mark.parametrize("dt", ["Lb0", "Lb1"])
 def test_gemm_kernel_structure(asm, cfg, dt):
-    sym, lines = _kernel_body(asm["ag_gemm.hip"], f"ag_gemm_kernelI{dt}ELi8ENS_8gemm_cfg3CfgILi{cfg}EEEE")
+    sym, lines = _kernel_body(asm["ag_gemm.hip"], f"ag_gemm_kernelI{dt}ELi8ENS_8gemm_cfg3CfgILi{cfg}E")
     first_barrier = next(i for i, ln in enumerate(lines) if ln.startswith("s_barrier"))
     # heap-base loads: all W of them before any tile or K-loop code (block layout may reorder the rest)
     assert sum(ln.startswith("s_load_dwordx2") for ln in lines[:first_barrier]) >= 8
@@ -132,7 +132,7 @@ def test_gemm_kernel_structure(asm, cfg, dt):
         i += 1
     mfma = [ln for ln in lines if ln.startswith("v_mfma")]
     assert mfma and all(ln.startswith("v_mfma_f32_16x16x32_" + ("bf16" if dt == "Lb1" else "f16")) for ln in mfma)
-    big = [(a, b) for a, b in runs if sum(lines[k].startswith("v_mfma") for k in range(a, b)) >= 16]
+    big = [(a, b) for a, b in runs if sum(lines[k].startswith("v_mfma") for k in range(a, b)) >= 8]
     assert big, "no MFMA run found"
     for a, b in big:
         seg = lines[a:b]
