@@ -536,8 +536,7 @@ ag_status_t ag_plan_gemm_all_gather(const ag_heap_geometry_t* geom, int W, int r
     p.tiles_n = static_cast<int64_t>(tiles_n);
     p.total_tiles = static_cast<int64_t>(total);
     p.n_programs = static_cast<int32_t>(std::min<uint64_t>(programs_req, total));
-    p.threads = 512;                                   // eight wave64s, two per SIMD
-    p.lds_bytes = 5 * (cfg->tm + cfg->tn) * 64;        // five ring slots of a 32-wide K stage
+    ag::gemm_resources(cfg->id, &p.threads, &p.lds_bytes);
     p.variant = cfg->id;
     *plan = p;
     return ok();

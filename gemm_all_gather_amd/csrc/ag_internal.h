@@ -61,5 +61,7 @@ struct GemmLaunch {
 };
 
 hipError_t launch_gemm(const GemmLaunch& l, hipStream_t stream);
+// Threads per workgroup and LDS bytes of a tile configuration (host-only arithmetic).
+void gemm_resources(int cfg, int* threads, int* lds_bytes);
 
 }  // namespace ag
