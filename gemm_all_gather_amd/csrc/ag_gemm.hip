@@ -73,6 +73,13 @@ __device__ inline void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 __device__ inline void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// s_waitcnt with only the LDS/scalar counter limited (at most N outstanding).
+template <int N>
+__device__ inline void wait_lgkmcnt()
+{
+    static_assert(N >= 0 && N < 16, "lgkmcnt is 4 bits");
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (N << 8));
+}
 
 template <bool BF16> struct Mfma;
 template <> struct Mfma<false> {
@@ -136,6 +143,7 @@ struct Cfg {
     static_assert(QROWS * C_PITCH <= STAGE && NSTG <= NS, "C staging must fit in the ring");
     static_assert(QROWS % 16 == 0, "a 16-row accumulator block never straddles two staging slots");
     static_assert(A_INSTR % NW == 0, "every wave issues the same number of A loads");
+    static_assert(BM + BN < 16, "one K-step's fragment reads fit the 4-bit LDS counter");
     static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "gfx950 has 160 KiB of LDS");
 };
 }  // namespace gemm_cfg
@@ -319,6 +327,12 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
                 const int f = f0 ^ (kk & 1);
                 if (kk + 1 < C::KSUB) {
                     read_frags(slot, kk + 1, f ^ 1);
+                    // the fragments of this K-step (read one step earlier,
+                    // possibly at the stage boundary) have landed; the reads
+                    // just issued may still be in flight
+                    __builtin_amdgcn_sched_barrier(0);
+                    wait_lgkmcnt<C::BM + C::BN>();
+                    __builtin_amdgcn_sched_barrier(0);
                 } else {
                     __builtin_amdgcn_sched_barrier(0);
                     wait_stages(std::integral_constant<int, C::NS - 2>{});

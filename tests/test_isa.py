@@ -148,6 +148,64 @@ def test_gemm_kernel_structure(asm, cfg, dt):
     assert not any(re.match(r"s_(cbranch|branch)", ln) for ln in seg)
 
 
+def _vregs(tok):
+    m = re.match(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _unguarded_fragment_uses(lines):
+    """MFMAs that read a register an LDS read may still be writing.
+
+    Walks the code in layout order (the fall-through path, which is how the
+    unrolled K loop is laid out): every ds_read joins a queue of pending
+    destination registers, s_waitcnt lgkmcnt(n) retires all but the newest n,
+    and an MFMA must not read any register still in the queue.  The hardware
+    does not interlock on LDS results, and the compiler does not count the
+    fragment reads written as inline assembly, so the kernel has to wait
+    explicitly.
+    """
+    pending, bad = [], []
+    for i, ln in enumerate(lines):
+        if ln.startswith("s_waitcnt"):
+            m = re.search(r"lgkmcnt\((\d+)\)", ln)
+            if m:
+                del pending[:max(0, len(pending) - int(m.group(1)))]
+        elif ln.startswith("ds_read"):
+            pending.append(_vregs(ln.split()[1].rstrip(",")))
+        elif ln.startswith("v_mfma"):
+            ops = [o.strip() for o in ln.split(None, 1)[1].split(",")]
+            src = _vregs(ops[1]) | _vregs(ops[2])
+            if any(p & src for p in pending):
+                bad.append((i, ln))
+    return bad
+
+
+@pytest.mark.parametrize("cfg", ["256ELi224", "256ELi256", "128ELi128"])
+@pytest.mark.parametrize("dt", ["Lb0", "Lb1"])
+@pytest.mark.parametrize("w", ["1", "8"])
+def test_gemm_fragments_waited_before_mfma(asm, cfg, dt, w):
+    _, lines = _kernel_body(asm["ag_gemm.hip"], f"ag_gemm_kernelI{dt}ELi{w}ENS_8gemm_cfg3CfgILi{cfg}E")
+    assert any(ln.startswith("ds_read_b128") for ln in lines)
+    bad = _unguarded_fragment_uses(lines)
+    assert not bad, bad[:3]
+
+
+def test_fragment_hazard_check_catches_a_missing_wait():
+    """The checker itself: a read consumed without a wait is flagged, a waited one is not."""
+    racy = ["ds_read_b128 v[2:5], v1", "ds_read_b128 v[6:9], v1 offset:64",
+            "v_mfma_f32_16x16x32_f16 v[10:13], v[2:5], v[6:9], v[10:13]"]
+    assert _unguarded_fragment_uses(racy)
+    partial = racy[:2] + ["s_waitcnt lgkmcnt(1)"] + racy[2:]
+    assert _unguarded_fragment_uses(partial)          # v[6:9] may still be landing
+    ok = racy[:2] + ["s_waitcnt lgkmcnt(0)"] + racy[2:]
+    assert not _unguarded_fragment_uses(ok)
+    newer = racy[:2] + ["s_waitcnt lgkmcnt(0)", "ds_read_b128 v[20:23], v1"] + racy[2:]
+    assert not _unguarded_fragment_uses(newer)         # an unrelated newer read may stay in flight
+
+
 def test_report_registers(asm, capsys):
     """Print VGPR/AGPR/SGPR/scratch/LDS per instantiation (reported next to timings)."""
     rows = []
