@@ -1,4 +1,4 @@
-"""CPU oracle for the multi-destination all-gather and the fused GEMM + all-gather.
+"""CPU oracle for the multi-destination all-gather, the all-to-all and the fused GEMM + all-gather.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke entry point and the
 benchmark's CPU-baseline leg may import this package.  The product path (the
@@ -14,6 +14,8 @@ from .ag_oracle import (  # noqa: F401
     all_gather_oracle,
     all_gather_expected_block,
     group_members,
+    all_to_all_oracle,
+    all_to_all_expected_block,
     round_f64_to_f16_bits,
     round_f64_to_bf16_bits,
     f16_bits_to_f64,

@@ -15,6 +15,12 @@ What it computes (sources are the three pages on the iris all-gather):
   heaps of ranks outside the group).  The tiled kernel, its destination order
   and its launch shape do not change this result, so the oracle is the
   definition itself, written as byte copies.
+* all-to-all -- ROCm/iris #594, "Compiler inspection and grouping", and
+  ROCm/iris #591, "Hoist the peer heap bases", name the all_to_all collective
+  as the next user of the same heap-base machinery; its result is that of
+  torch.distributed.all_to_all_single with equal splits: every rank's input
+  is W chunks, chunk j goes to member j, and member j's output holds, in
+  group order, the chunk j of every rank.  Written as byte copies.
 * fused GEMM + all-gather -- ROCm/iris #626, "Summary" and "Assembly" table
   (256x256 fp16 C tile produced by the matmul and stored to every rank): each
   rank's C_j = A_j . B_j, rounded once to the 16-bit output type, then
@@ -91,6 +97,43 @@ def all_gather_oracle(slab: np.ndarray, region_bytes: int, inputs: list[np.ndarr
             n = blocks[j].size
             out[cursor:cursor + n] = blocks[j]
             cursor += n
+    return out
+
+
+# ---------------------------------------------------------------------------
+# all-to-all
+# ---------------------------------------------------------------------------
+
+def all_to_all_expected_block(inputs: list[np.ndarray], j: int) -> np.ndarray:
+    """What group member j must hold: chunk j of every rank's input, in group order.
+
+    inputs[g] is group rank g's (W*M_chunk, N) array, chunk c being rows
+    [c*M_chunk, (c+1)*M_chunk) (all_to_all_single with equal splits).
+    """
+    world = len(inputs)
+    parts = []
+    for x in inputs:
+        x = np.asarray(x)
+        m = x.shape[0] // world
+        parts.append(x[j * m:(j + 1) * m])
+    return np.concatenate(parts, axis=0)
+
+
+def all_to_all_oracle(slab: np.ndarray, region_bytes: int, inputs: list[np.ndarray],
+                      rank_start: int, rank_stride: int, out_offset: int) -> np.ndarray:
+    """Full-heap result of an all-to-all by every member of a group.
+
+    Same conventions as all_gather_oracle; inputs[g] holds W chunks.  In member
+    j's region the W*M_chunk*N*e bytes at out_offset hold
+    all_to_all_expected_block(inputs, j); every other byte is unchanged.
+    """
+    slab = np.asarray(slab, dtype=np.uint8)
+    out = slab.copy()
+    members = group_members(rank_start, rank_stride, len(inputs))
+    for j, h in enumerate(members):
+        block = np.ascontiguousarray(all_to_all_expected_block(inputs, j)).view(np.uint8).reshape(-1)
+        start = h * region_bytes + out_offset
+        out[start:start + block.size] = block
     return out
 
 

@@ -14,6 +14,7 @@ import torch
 from oracle import (
     F16, BF16,
     all_gather_oracle, all_gather_expected_block, group_members,
+    all_to_all_oracle, all_to_all_expected_block,
     round_f64_to_f16_bits, round_f64_to_bf16_bits, f16_bits_to_f64, bf16_bits_to_f64,
     gemm_oracle, gemm_oracle_entries, gemm_all_gather_oracle,
 )
@@ -55,6 +56,79 @@ def test_all_gather_hand_worked_strided_example(golden_dir):
                             kv["out_offset_bytes"]).view(np.uint16).reshape(R, words)
     for r in range(R):
         assert out[r].tolist() == expect[r], f"region {r}"
+
+
+def _run_fixture(path, oracle_fn, mkey):
+    rows = _read_fixture(path)
+    kv, inputs, expect = {}, {}, {}
+    for r in rows:
+        if r[0] == "input":
+            inputs[int(r[1])] = [int(v) for v in r[2:]]
+        elif r[0] == "expect":
+            expect[int(r[1])] = [S16 if v == "S" else int(v) for v in r[2:]]
+        else:
+            kv[r[0]] = int(r[1])
+    R, words = kv["regions"], kv["region_words"]
+    M, N = kv[mkey], kv["n"]
+    slab = np.full(R * words, S16, dtype=np.uint16).view(np.uint8)
+    ins = [np.array(inputs[j], dtype=np.uint16).reshape(-1, N) for j in sorted(inputs)]
+    assert all(x.shape[0] in (M, M * len(ins)) for x in ins)
+    out = oracle_fn(slab, words * 2, ins, kv["rank_start"], kv["rank_stride"],
+                    kv["out_offset_bytes"]).view(np.uint16).reshape(R, words)
+    for r in range(R):
+        assert out[r].tolist() == expect[r], f"region {r}"
+
+
+@pytest.mark.parametrize("name", ["all_to_all_strided_tiny.txt", "all_to_all_w3_tiny.txt"])
+def test_all_to_all_hand_worked_examples(golden_dir, name):
+    _run_fixture(os.path.join(golden_dir, name), all_to_all_oracle, "m_chunk")
+
+
+@pytest.mark.parametrize("W,M,N", [(1, 3, 4), (2, 1, 1), (3, 2, 5), (8, 4, 7)])
+def test_all_to_all_is_a_block_transpose(W, M, N):
+    """Library routine: the result is the (rank, chunk) block matrix transposed.
+
+    Stacking every rank's chunks as X[g, c] and swapping the two block axes
+    gives Y[j, g] = X[g, j], member j's output in group order.
+    """
+    ins = [gen.random_bit_patterns((W * M, N), 2, 31, W, g) for g in range(W)]
+    X = np.stack([x.reshape(W, M, N) for x in ins])          # X[g, c, m, n]
+    Y = np.swapaxes(X, 0, 1)                                  # Y[j, g, m, n]
+    for j in range(W):
+        assert np.array_equal(all_to_all_expected_block(ins, j), Y[j].reshape(W * M, N))
+
+
+@pytest.mark.parametrize("W,start,stride", [(2, 0, 1), (3, 1, 2), (4, 0, 2), (8, 0, 1)])
+def test_all_to_all_twice_is_the_identity_and_leaves_the_rest(W, start, stride):
+    """Invariants: the exchange is an involution, and only member output blocks change."""
+    M, N, e = 3, 6, 2
+    R = start + (W - 1) * stride + 2
+    blk = M * N * e
+    region = W * blk + 96
+    off = 32
+    slab = gen.random_bit_patterns((R * region // 2,), 2, 17, W, R).view(np.uint8)
+    ins = [gen.uniform_pm1((W * M, N), "f16", 5, g) for g in range(W)]
+    out = all_to_all_oracle(slab, region, ins, start, stride, off)
+    members = group_members(start, stride, W)
+    # member outputs, fed back in as inputs, return the original inputs
+    outs = [out[h * region + off:h * region + off + W * blk].view(np.uint16).reshape(W * M, N) for h in members]
+    back = all_to_all_oracle(out, region, outs, start, stride, off)
+    for g, h in enumerate(members):
+        got = back[h * region + off:h * region + off + W * blk].view(np.uint16).reshape(W * M, N)
+        assert np.array_equal(got, ins[g].view(np.uint16))
+    # every byte outside the member output blocks is unchanged
+    mask = np.ones(R * region, dtype=bool)
+    for h in members:
+        mask[h * region + off:h * region + off + W * blk] = False
+    assert np.array_equal(out[mask], slab[mask])
+
+
+def test_all_to_all_single_rank_is_a_copy():
+    x = gen.uniform_pm1((5, 9), "bf16", 3, 0)
+    slab = np.zeros(4096, dtype=np.uint8)
+    out = all_to_all_oracle(slab, 4096, [x], 0, 1, 128)
+    assert np.array_equal(out[128:128 + x.nbytes], x.view(np.uint8).reshape(-1))
+    assert not out[:128].any() and not out[128 + x.nbytes:].any()
 
 
 def test_group_members_strided():
