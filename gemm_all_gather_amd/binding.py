@@ -47,10 +47,27 @@ class Plan(ctypes.Structure):
                 ("vectors_per_thread", ctypes.c_int32), ("variant", ctypes.c_int32),
                 ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("total_tiles", ctypes.c_int64),
                 ("rank_block_offset", ctypes.c_uint64), ("bytes_read", ctypes.c_uint64),
-                ("bytes_written", ctypes.c_uint64), ("flops", ctypes.c_double)]
+                ("bytes_written", ctypes.c_uint64), ("flops", ctypes.c_double),
+                ("dest_group", ctypes.c_int32), ("schedule", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+AG_SCHEDULE_TILES, AG_SCHEDULE_PARTITIONED = 0, 1
+SCHEDULES = {"tiles": AG_SCHEDULE_TILES, "partitioned": AG_SCHEDULE_PARTITIONED}
+
+
+class CopyOptions(ctypes.Structure):
+    _fields_ = [("dest_group", ctypes.c_int32), ("schedule", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
+
+
+def _options(dest_group=0, schedule=0) -> CopyOptions:
+    o = CopyOptions()
+    o.dest_group = dest_group
+    o.schedule = SCHEDULES[schedule] if isinstance(schedule, str) else schedule
+    return o
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -71,6 +88,14 @@ _SIGNATURES = {
     "ag_all_gather": [_vp, _c_int, _c_int, _c_int, _vp, _c_size, _c_i64, _c_i64, _c_int, _c_int, _c_int,
                       _c_int, _vp],
     "ag_plan_all_gather": [ctypes.POINTER(Geometry), _c_int, _c_int, _c_int, _c_u64, _c_size, _c_i64, _c_i64,
+                           _c_int, _c_int, _c_int, _c_int, ctypes.POINTER(Plan)],
+    "ag_all_gather_ex": [_vp, _c_int, _c_int, _c_int, _vp, _c_size, _c_i64, _c_i64, _c_int, _c_int, _c_int,
+                         _c_int, ctypes.POINTER(CopyOptions), _vp],
+    "ag_plan_all_gather_ex": [ctypes.POINTER(Geometry), _c_int, _c_int, _c_int, _c_u64, _c_size, _c_i64, _c_i64,
+                              _c_int, _c_int, _c_int, _c_int, ctypes.POINTER(CopyOptions), ctypes.POINTER(Plan)],
+    "ag_all_to_all": [_vp, _c_int, _c_int, _c_int, _vp, _c_size, _c_i64, _c_i64, _c_int, _c_int, _c_int,
+                      _c_int, _vp],
+    "ag_plan_all_to_all": [ctypes.POINTER(Geometry), _c_int, _c_int, _c_int, _c_u64, _c_size, _c_i64, _c_i64,
                            _c_int, _c_int, _c_int, _c_int, ctypes.POINTER(Plan)],
     "ag_gemm_all_gather": [_vp, _c_int, _c_int, _c_int, _vp, _c_i64, _vp, _c_i64, _c_size, _c_i64, _c_i64,
                            _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int, _vp],
@@ -218,6 +243,39 @@ def all_gather(heap: Heap, W, rank_start, rank_stride, input, out_offset, M_loca
                tile_m=0, tile_n=0, n_programs=0, stream=None) -> None:
     _check(lib().ag_all_gather(heap.handle, W, rank_start, rank_stride, _ptr(input), out_offset, M_local, N,
                                _dtype(dtype), tile_m, tile_n, n_programs, _stream(stream)), "ag_all_gather")
+
+
+def plan_all_gather_ex(geom: Geometry, W, rank_start, rank_stride, input_addr, out_offset, M_local, N, dtype,
+                       tile_m=0, tile_n=0, n_programs=0, dest_group=0, schedule=0) -> Plan:
+    p = Plan()
+    o = _options(dest_group, schedule)
+    _check(lib().ag_plan_all_gather_ex(ctypes.byref(geom), W, rank_start, rank_stride, _ptr(input_addr), out_offset,
+                                       M_local, N, _dtype(dtype), tile_m, tile_n, n_programs, ctypes.byref(o),
+                                       ctypes.byref(p)), "ag_plan_all_gather_ex")
+    return p
+
+
+def all_gather_ex(heap: Heap, W, rank_start, rank_stride, input, out_offset, M_local, N, dtype,
+                  tile_m=0, tile_n=0, n_programs=0, dest_group=0, schedule=0, stream=None) -> None:
+    o = _options(dest_group, schedule)
+    _check(lib().ag_all_gather_ex(heap.handle, W, rank_start, rank_stride, _ptr(input), out_offset, M_local, N,
+                                  _dtype(dtype), tile_m, tile_n, n_programs, ctypes.byref(o), _stream(stream)),
+           "ag_all_gather_ex")
+
+
+def plan_all_to_all(geom: Geometry, W, rank_start, rank_stride, input_addr, out_offset, M_chunk, N, dtype,
+                    tile_m=0, tile_n=0, n_programs=0) -> Plan:
+    p = Plan()
+    _check(lib().ag_plan_all_to_all(ctypes.byref(geom), W, rank_start, rank_stride, _ptr(input_addr), out_offset,
+                                    M_chunk, N, _dtype(dtype), tile_m, tile_n, n_programs, ctypes.byref(p)),
+           "ag_plan_all_to_all")
+    return p
+
+
+def all_to_all(heap: Heap, W, rank_start, rank_stride, input, out_offset, M_chunk, N, dtype,
+               tile_m=0, tile_n=0, n_programs=0, stream=None) -> None:
+    _check(lib().ag_all_to_all(heap.handle, W, rank_start, rank_stride, _ptr(input), out_offset, M_chunk, N,
+                               _dtype(dtype), tile_m, tile_n, n_programs, _stream(stream)), "ag_all_to_all")
 
 
 def plan_gemm_all_gather(geom: Geometry, W, rank_start, rank_stride, a_addr, lda, b_addr, ldb, out_offset,

@@ -24,6 +24,18 @@
 //   * the next tile's loads are issued before the current tile's stores, so
 //     waiting for them never waits for the stores (the memory counter is in
 //     issue order), and no destination store is preceded by a full drain.
+//
+// Variants (ROCm/iris #594, "Reviewer performance evaluation" and "Compiler
+// inspection and grouping"; ROCm/iris #591, "INLINE grouping"; ROCm/iris
+// #626, "Triton CCL all-gather" on the partitioned kernel):
+//   * destination groups (G > 0): after every G destinations' stores, wait
+//     until everything issued before that group has completed, so at most
+//     two groups of stores are in flight;
+//   * partitioned schedule: program p stores only to destination p % W
+//     (rotated order, 0 = local) and walks every (grid/W)-th tile from
+//     p / W, reading each input tile once per destination;
+//   * all-to-all (ag_a2a_kernel): for each tile, destination i receives
+//     the tile of input chunk (g + i) mod W, the chunk meant for it.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -50,6 +62,14 @@ constexpr int kRawBufferWord3 = 0x00020000;
 // A lane offset that is always past num_records (<= 0x7fffffff): the access
 // is dropped by the hardware (store) or returns zero (load).
 constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
+template <int N>
+__device__ inline void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(uint64_t base, uint32_t num_records)
 {
@@ -86,23 +106,34 @@ struct TileRef {
     uint32_t col0;       // byte column of the tile's first element
 };
 
-template <int VEC, int W, int VPT>
+// Heap base of group member (g + i) mod world.
+__device__ inline uint64_t member_base(const CopyKernelArgs& a, int i)
+{
+    // g < world and i < 2*world: two conditional subtractions reduce mod world
+    int gi = a.group_rank + i;
+    if (gi >= static_cast<int>(a.world)) gi -= a.world;
+    if (gi >= static_cast<int>(a.world)) gi -= a.world;
+    return __builtin_nontemporal_load(a.heap_bases + (a.rank_start + gi * a.rank_stride));
+}
+
+// W destinations per tile (W = 1 when partitioned); G destinations per wait
+// (0: none).
+template <int VEC, int W, int VPT, int G>
 __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
 {
     using VT = Vec<VEC>;
     using V = typename VT::T;
+    static_assert(G == 0 || G < W, "a group smaller than the destination count");
 
     // ---- prologue: translate every destination once, before the tile loop.
-    // All W table entries are requested before any is used, so the scalar
-    // loads overlap and the prologue pays one memory latency.
+    // All table entries are requested before any is used, so the scalar
+    // loads overlap and the prologue pays one memory latency.  A partitioned
+    // program owns destination p % world of the rotated order.
+    const int first = a.partitioned ? static_cast<int>(blockIdx.x % a.world) : 0;
+    const uint64_t local_base = __builtin_nontemporal_load(a.heap_bases + a.rank);
     uint64_t base[W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) {
-        int gi = a.group_rank + i;
-        if (gi >= W) gi -= W;
-        base[i] = __builtin_nontemporal_load(a.heap_bases + (a.rank_start + gi * a.rank_stride));
-    }
-    const uint64_t local_base = base[0];   // i = 0 is the calling rank itself
+    for (int i = 0; i < W; ++i) base[i] = member_base(a, first + i);
     const uint64_t out_local = local_base + a.rank_block_offset;
     uint64_t dest[W];   // out_local + (dest_base - local_base): local region first, then rotated peers
 #pragma unroll
@@ -124,8 +155,9 @@ __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
         lane_off[j] = (idx >> a.vecs_per_row_log2) * static_cast<uint32_t>(a.row_bytes) + lane_col[j];
     }
 
-    const uint32_t stride = gridDim.x * a.slices;
-    uint32_t t = blockIdx.x * a.slices + slice;
+    // partitioned: the programs of one destination walk the tiles among themselves
+    const uint32_t stride = a.partitioned ? gridDim.x / a.world : gridDim.x * a.slices;
+    uint32_t t = a.partitioned ? blockIdx.x / a.world : blockIdx.x * a.slices + slice;
     if (t >= a.total_tiles) return;
 
     // Tile -> (tm, tn), row-major over tiles.  Rows past M_local fall past the
@@ -158,6 +190,8 @@ __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
             const __amdgpu_buffer_rsrc_t dst = make_rsrc(dest[i] + r.off, r.records);
 #pragma unroll
             for (int j = 0; j < VPT; ++j) VT::store(v[j], dst, vo[j]);
+            // end of a destination group: retire everything issued before it
+            if (G > 0 && (i + 1) % G == 0 && i + 1 < W) wait_vmcnt<G * VPT>();
         }
     };
 
@@ -202,53 +236,216 @@ __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
     }
 }
 
+// All-to-all: tile t of every input chunk is loaded (chunk (g + i) mod W
+// for destination i), then tile t of destination i's block receives it,
+// local region first, then the rotated peers.  The W chunk tiles of the next
+// tile are loaded before the current ones are stored.
+template <int VEC, int W, int VPT>
+__global__ __launch_bounds__(256) void ag_a2a_kernel(CopyKernelArgs a)
+{
+    using VT = Vec<VEC>;
+    using V = typename VT::T;
+
+    const uint64_t local_base = __builtin_nontemporal_load(a.heap_bases + a.rank);
+    uint64_t dest[W];   // destination i = group member (g + i) mod W
+    uint64_t src[W];    // input chunk meant for destination i
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+        int gi = a.group_rank + i;
+        if (gi >= W) gi -= W;
+        const uint64_t b = __builtin_nontemporal_load(a.heap_bases + (a.rank_start + gi * a.rank_stride));
+        dest[i] = local_base + a.rank_block_offset + static_cast<uint64_t>(static_cast<int64_t>(b - local_base));
+        src[i] = reinterpret_cast<uint64_t>(a.input) + static_cast<uint64_t>(gi) * a.chunk_bytes;
+    }
+    const uint64_t block_bytes = a.chunk_bytes;
+
+    const uint32_t lane = threadIdx.x;
+    const uint32_t vpr_mask = (1u << a.vecs_per_row_log2) - 1u;
+    uint32_t lane_off[VPT], lane_col[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const uint32_t idx = lane + 256u * j;
+        lane_col[j] = (idx & vpr_mask) * VEC;
+        lane_off[j] = (idx >> a.vecs_per_row_log2) * static_cast<uint32_t>(a.row_bytes) + lane_col[j];
+    }
+    const uint32_t stride = gridDim.x;
+    uint32_t t = blockIdx.x;
+    if (t >= a.total_tiles) return;
+
+    auto origin = [&](uint32_t tile, bool valid) {
+        TileRef r;
+        const uint32_t tm = tile / a.tiles_n;
+        const uint32_t tn = tile - tm * a.tiles_n;
+        r.col0 = tn * a.tile_row_bytes;
+        r.off = static_cast<uint64_t>(tm) * a.tile_m * a.row_bytes + r.col0;
+        const uint64_t left = valid ? block_bytes - r.off : 0;
+        r.records = static_cast<uint32_t>(left < 0x7fffffffull ? left : 0x7fffffffull);
+        r.full = r.col0 + a.tile_row_bytes <= a.row_bytes;
+        return r;
+    };
+    auto offsets = [&](const TileRef& r, uint32_t (&vo)[VPT]) {
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+            vo[j] = (r.full || r.col0 + lane_col[j] < a.row_bytes) ? lane_off[j] : kOutOfRange;
+    };
+    auto load_tile = [&](const TileRef& r, const uint32_t (&vo)[VPT], V (&v)[W][VPT]) {
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            const __amdgpu_buffer_rsrc_t s = make_rsrc(src[i] + r.off, r.records);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) v[i][j] = VT::load(s, vo[j]);
+        }
+    };
+    auto store_tile = [&](const TileRef& r, const uint32_t (&vo)[VPT], const V (&v)[W][VPT]) {
+#pragma unroll
+        for (int i = 0; i < W; ++i) {   // local region first, then the rotated peers
+            const __amdgpu_buffer_rsrc_t d = make_rsrc(dest[i] + r.off, r.records);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) VT::store(v[i][j], d, vo[j]);
+        }
+    };
+
+    // same two-register-set pipeline as the all-gather loop
+    TileRef ta = origin(t, true), tb;
+    uint32_t oa[VPT], ob[VPT];
+    V va[W][VPT], vb[W][VPT];
+    offsets(ta, oa);
+    load_tile(ta, oa, va);
+    uint32_t tn = t + stride;
+    bool more = tn < a.total_tiles && tn > t;
+    tb = origin(more ? tn : t, more);
+    offsets(tb, ob);
+    load_tile(tb, ob, vb);
+    store_tile(ta, oa, va);
+    if (!more) return;
+    t = tn;
+    for (;;) {
+        tn = t + stride;
+        more = tn < a.total_tiles && tn > t;
+        ta = origin(more ? tn : t, more);
+        offsets(ta, oa);
+        load_tile(ta, oa, va);
+        store_tile(tb, ob, vb);
+        if (!more) break;
+        t = tn;
+
+        tn = t + stride;
+        more = tn < a.total_tiles && tn > t;
+        tb = origin(more ? tn : t, more);
+        offsets(tb, ob);
+        load_tile(tb, ob, vb);
+        store_tile(ta, oa, va);
+        if (!more) break;
+        t = tn;
+    }
+}
+
 using CopyFn = void (*)(CopyKernelArgs);
 
+// ---- all-gather instantiations: VEC x W x VPT, destination groups G for
+// 16- and 8-byte vectors (G < W)
+template <int VEC, int W, int VPT>
+CopyFn pick_group(int g)
+{
+    if (g == 0) return ag_copy_kernel<VEC, W, VPT, 0>;
+    if constexpr (VEC >= 8) {
+        if constexpr (W > 1) if (g == 1) return ag_copy_kernel<VEC, W, VPT, 1>;
+        if constexpr (W > 2) if (g == 2) return ag_copy_kernel<VEC, W, VPT, 2>;
+        if constexpr (W > 4) if (g == 4) return ag_copy_kernel<VEC, W, VPT, 4>;
+    }
+    return nullptr;
+}
+
 template <int VEC, int W>
-CopyFn pick_vpt(int vpt)
+CopyFn pick_vpt(int vpt, int g)
 {
     switch (vpt) {
-    case 1: return ag_copy_kernel<VEC, W, 1>;
-    case 2: return ag_copy_kernel<VEC, W, 2>;
-    case 4: return ag_copy_kernel<VEC, W, 4>;
-    case 8: return ag_copy_kernel<VEC, W, 8>;
+    case 1: return pick_group<VEC, W, 1>(g);
+    case 2: return pick_group<VEC, W, 2>(g);
+    case 4: return pick_group<VEC, W, 4>(g);
+    case 8: return pick_group<VEC, W, 8>(g);
     default: return nullptr;
     }
 }
 
 template <int VEC>
-CopyFn pick_world(int w, int vpt)
+CopyFn pick_world(int w, int vpt, int g)
 {
     switch (w) {
-    case 1: return pick_vpt<VEC, 1>(vpt);
-    case 2: return pick_vpt<VEC, 2>(vpt);
-    case 3: return pick_vpt<VEC, 3>(vpt);
-    case 4: return pick_vpt<VEC, 4>(vpt);
-    case 5: return pick_vpt<VEC, 5>(vpt);
-    case 6: return pick_vpt<VEC, 6>(vpt);
-    case 7: return pick_vpt<VEC, 7>(vpt);
-    case 8: return pick_vpt<VEC, 8>(vpt);
+    case 1: return pick_vpt<VEC, 1>(vpt, g);
+    case 2: return pick_vpt<VEC, 2>(vpt, g);
+    case 3: return pick_vpt<VEC, 3>(vpt, g);
+    case 4: return pick_vpt<VEC, 4>(vpt, g);
+    case 5: return pick_vpt<VEC, 5>(vpt, g);
+    case 6: return pick_vpt<VEC, 6>(vpt, g);
+    case 7: return pick_vpt<VEC, 7>(vpt, g);
+    case 8: return pick_vpt<VEC, 8>(vpt, g);
     default: return nullptr;
     }
 }
 
-CopyFn pick_kernel(int vec, int w, int vpt)
+// ---- all-to-all instantiations: VEC x W x VPT (VPT <= 2)
+template <int VEC, int W>
+CopyFn pick_a2a_vpt(int vpt)
 {
+    switch (vpt) {
+    case 1: return ag_a2a_kernel<VEC, W, 1>;
+    case 2: return ag_a2a_kernel<VEC, W, 2>;
+    default: return nullptr;
+    }
+}
+
+template <int VEC>
+CopyFn pick_a2a_world(int w, int vpt)
+{
+    switch (w) {
+    case 1: return pick_a2a_vpt<VEC, 1>(vpt);
+    case 2: return pick_a2a_vpt<VEC, 2>(vpt);
+    case 3: return pick_a2a_vpt<VEC, 3>(vpt);
+    case 4: return pick_a2a_vpt<VEC, 4>(vpt);
+    case 5: return pick_a2a_vpt<VEC, 5>(vpt);
+    case 6: return pick_a2a_vpt<VEC, 6>(vpt);
+    case 7: return pick_a2a_vpt<VEC, 7>(vpt);
+    case 8: return pick_a2a_vpt<VEC, 8>(vpt);
+    default: return nullptr;
+    }
+}
+
+CopyFn pick_kernel(int kind, int vec, int w, int g, int vpt)
+{
+    if (kind == kCopyAllToAll) {
+        if (g != 0) return nullptr;
+        switch (vec) {
+        case 16: return pick_a2a_world<16>(w, vpt);
+        case 8: return pick_a2a_world<8>(w, vpt);
+        case 4: return pick_a2a_world<4>(w, vpt);
+        case 2: return pick_a2a_world<2>(w, vpt);
+        default: return nullptr;
+        }
+    }
     switch (vec) {
-    case 16: return pick_world<16>(w, vpt);
-    case 8: return pick_world<8>(w, vpt);
-    case 4: return pick_world<4>(w, vpt);
-    case 2: return pick_world<2>(w, vpt);
+    case 16: return pick_world<16>(w, vpt, g);
+    case 8: return pick_world<8>(w, vpt, g);
+    case 4: return pick_world<4>(w, vpt, g);
+    case 2: return pick_world<2>(w, vpt, g);
     default: return nullptr;
     }
 }
 
 }  // namespace
 
+bool copy_supported(int kind, int vec_bytes, int dests, int group, int vpt)
+{
+    return pick_kernel(kind, vec_bytes, dests, group, vpt) != nullptr;
+}
+
 hipError_t launch_copy(const CopyLaunch& l, hipStream_t stream)
 {
-    CopyFn fn = pick_kernel(l.vec_bytes, l.world, l.vpt);
-    if (fn == nullptr || l.args.slices < 1 || l.args.slices > 4 || l.grid < 1)
+    CopyFn fn = pick_kernel(l.kind, l.vec_bytes, l.dests, l.group, l.vpt);
+    const uint32_t max_slices = l.kind == kCopyAllToAll ? 1 : 4;
+    if (fn == nullptr || l.args.slices < 1 || l.args.slices > max_slices || l.grid < 1 || l.args.world < 1)
+        return hipErrorInvalidValue;
+    if (l.args.partitioned && (l.args.slices != 1 || l.dests != 1 || l.grid % l.args.world != 0))
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3(l.grid), dim3(256 * l.args.slices), 0, stream, l.args);
     return hipGetLastError();

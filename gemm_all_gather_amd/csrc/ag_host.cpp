@@ -299,25 +299,45 @@ ag_status_t ag_heap_geometry(const ag_heap_t* heap, ag_heap_geometry_t* geom)
 }
 
 // ---------------------------------------------------------------------------
-// all-gather
+// all-gather (default, grouped, partitioned) and all-to-all: one planner
 // ---------------------------------------------------------------------------
 
-ag_status_t ag_plan_all_gather(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
-                               uint64_t input_addr, size_t out_offset, int64_t M_local, int64_t N,
-                               ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, ag_plan_t* plan)
+}  // extern "C"
+
+namespace {
+
+// Validation and launch decisions shared by every copy entry point.  kind:
+// ag::kCopyAllGather (M = M_local rows per rank) or ag::kCopyAllToAll (M =
+// M_chunk rows per chunk, W chunks in the input).
+ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_start, int rank_stride,
+                      uint64_t input_addr, size_t out_offset, int64_t M, int64_t N, ag_dtype_t dtype, int tile_m,
+                      int tile_n, int n_programs, const ag_copy_options_t* options, ag_plan_t* plan)
 {
     ag_status_t s = check_geometry(geom);
     if (s != AG_OK) return s;
     if (!plan) return fail(AG_ERR_INVALID_ARG, "plan is NULL");
+    const bool a2a = kind == ag::kCopyAllToAll;
+    const char* mname = a2a ? "M_chunk" : "M_local";
+    ag_copy_options_t opt{};
+    if (options) opt = *options;
+    for (int i = 0; i < 6; ++i)
+        if (opt.reserved[i] != 0) return fail(AG_ERR_INVALID_ARG, "options->reserved[%d] is not 0", i);
+    if (opt.schedule != AG_SCHEDULE_TILES && opt.schedule != AG_SCHEDULE_PARTITIONED)
+        return fail(AG_ERR_INVALID_ARG, "unknown schedule %d", opt.schedule);
+    if (opt.dest_group < 0) return fail(AG_ERR_INVALID_ARG, "dest_group %d < 0", opt.dest_group);
+    if (opt.dest_group != 0 && opt.dest_group != 1 && opt.dest_group != 2 && opt.dest_group != 4)
+        return fail(AG_ERR_UNSUPPORTED, "dest_group %d: 0, 1, 2 or 4 are supported", opt.dest_group);
+    if (opt.schedule == AG_SCHEDULE_PARTITIONED && opt.dest_group != 0)
+        return fail(AG_ERR_INVALID_ARG, "a partitioned program has one destination: dest_group must be 0");
     int g = 0;
     s = check_group(geom, W, rank_start, rank_stride, &g);
     if (s != AG_OK) return s;
     const int e = elem_bytes(dtype);
     if (e == 0) return fail(AG_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
-    if (M_local < 0) return fail(AG_ERR_INVALID_ARG, "M_local %lld < 0", static_cast<long long>(M_local));
+    if (M < 0) return fail(AG_ERR_INVALID_ARG, "%s %lld < 0", mname, static_cast<long long>(M));
     if (N < 1) return fail(AG_ERR_INVALID_ARG, "N %lld < 1", static_cast<long long>(N));
-    if (M_local > (int64_t{1} << 31) - 1 || N > (int64_t{1} << 31) - 1)
-        return fail(AG_ERR_UNSUPPORTED, "M_local or N >= 2^31");
+    if (M > (int64_t{1} << 31) - 1 || N > (int64_t{1} << 31) - 1)
+        return fail(AG_ERR_UNSUPPORTED, "%s or N >= 2^31", mname);
     if (n_programs < 0) return fail(AG_ERR_INVALID_ARG, "n_programs %d < 0", n_programs);
     if (tile_m == 0 && tile_n == 0) {
         tile_m = 8;
@@ -329,7 +349,7 @@ ag_status_t ag_plan_all_gather(const ag_heap_geometry_t* geom, int W, int rank_s
         return fail(AG_ERR_UNSUPPORTED, "tile %dx%d: tile_m must be a power of two <= 256 and tile_n a power of two in [8, 4096]",
                     tile_m, tile_n);
     const uint64_t row_bytes = static_cast<uint64_t>(N) * e;
-    const uint64_t blk = static_cast<uint64_t>(M_local) * row_bytes;
+    const uint64_t blk = static_cast<uint64_t>(M) * row_bytes;   // this rank's rows in every output block
     if (out_offset % e != 0)
         return fail(AG_ERR_INVALID_ARG, "out_offset %zu is not a multiple of the element size %d", out_offset, e);
     if (blk > geom->bytes_per_rank / W || out_offset > geom->bytes_per_rank - W * blk)
@@ -337,29 +357,34 @@ ag_status_t ag_plan_all_gather(const ag_heap_geometry_t* geom, int W, int rank_s
                     W, static_cast<unsigned long long>(blk), out_offset,
                     static_cast<unsigned long long>(geom->bytes_per_rank));
 
+    const bool part = !a2a && opt.schedule == AG_SCHEDULE_PARTITIONED;
+    const uint64_t in_bytes = a2a ? W * blk : blk;
     ag_plan_t p{};
     p.group_rank = g;
     p.tile_m = tile_m;
     p.tile_n = tile_n;
     p.threads = 256;
     p.rank_block_offset = out_offset + static_cast<uint64_t>(g) * blk;
-    p.bytes_read = blk;
-    p.bytes_written = blk * W;
-    if (M_local == 0) {   // nothing to move: valid no-op
+    p.bytes_read = part ? W * blk : in_bytes;
+    p.bytes_written = W * blk;
+    p.schedule = part ? AG_SCHEDULE_PARTITIONED : AG_SCHEDULE_TILES;
+    p.dest_group = (!a2a && opt.dest_group < W) ? opt.dest_group : 0;
+    if (a2a && opt.dest_group != 0) return fail(AG_ERR_INVALID_ARG, "the all-to-all takes no destination groups");
+    if (M == 0) {   // nothing to move: valid no-op
         *plan = p;
         return ok();
     }
     if (input_addr == 0) return fail(AG_ERR_INVALID_ARG, "input is NULL");
     if (input_addr % e != 0) return fail(AG_ERR_INVALID_ARG, "input is not aligned to the element size");
 
-    // input must not overlap any member's output block, except being exactly
-    // this rank's own rows in its own region
+    // The input must not overlap any member's output block; the all-gather
+    // input may be exactly this rank's own rows in its own region (in place).
     const uint64_t own = geom->slab_addr + static_cast<uint64_t>(geom->rank) * geom->bytes_per_rank + p.rank_block_offset;
-    if (input_addr != own) {
+    if (a2a || input_addr != own) {
         for (int j = 0; j < W; ++j) {
             const uint64_t region = geom->slab_addr +
                 static_cast<uint64_t>(rank_start + j * rank_stride) * geom->bytes_per_rank;
-            if (overlaps(input_addr, blk, region + out_offset, W * blk))
+            if (overlaps(input_addr, in_bytes, region + out_offset, W * blk))
                 return fail(AG_ERR_INVALID_ARG, "input overlaps the output block of region %d", rank_start + j * rank_stride);
         }
     }
@@ -370,53 +395,70 @@ ag_status_t ag_plan_all_gather(const ag_heap_geometry_t* geom, int W, int rank_s
     while (vec > e && ((row_bytes % vec) != 0 || (input_addr % vec) != 0 || (out_addr % vec) != 0)) vec /= 2;
     const uint64_t tile_row_bytes = static_cast<uint64_t>(tile_n) * e;
     const uint64_t tile_vecs = static_cast<uint64_t>(tile_m) * tile_row_bytes / vec;
-    if (tile_vecs % 256 != 0 || tile_vecs / 256 > kCopyMaxVpt)
+    const int max_vpt = a2a ? 2 : kCopyMaxVpt;
+    if (tile_vecs % 256 != 0 || tile_vecs / 256 > static_cast<uint64_t>(max_vpt))
         return fail(AG_ERR_UNSUPPORTED, "tile %dx%d holds %llu %d-byte vectors; 256 to %d are supported",
-                    tile_m, tile_n, static_cast<unsigned long long>(tile_vecs), vec, 256 * kCopyMaxVpt);
+                    tile_m, tile_n, static_cast<unsigned long long>(tile_vecs), vec, 256 * max_vpt);
     if (static_cast<uint64_t>(tile_m) * row_bytes >= (uint64_t{1} << 31))
         return fail(AG_ERR_UNSUPPORTED, "a tile spans 2 GiB or more of the input");
+    if (p.dest_group > 0 && vec < 8)
+        return fail(AG_ERR_UNSUPPORTED, "destination groups need 16- or 8-byte vectors (this call gets %d)", vec);
 
-    const uint64_t tiles_m = ceil_div(M_local, tile_m);
+    const uint64_t tiles_m = ceil_div(M, tile_m);
     const uint64_t tiles_n = ceil_div(N, tile_n);
     const uint64_t total = tiles_m * tiles_n;
     if (total >= (uint64_t{1} << 31)) return fail(AG_ERR_UNSUPPORTED, "more than 2^31 tiles");
 
     const uint64_t programs = n_programs == 0 ? geom->num_cus : n_programs;
-    // concurrent tiles per program: up to kCopyMaxSlices while every slice still gets a tile
-    uint64_t slices = 1;
-    while (slices < static_cast<uint64_t>(kCopyMaxSlices) && programs * slices * 2 <= total) slices *= 2;
-    const uint64_t grid = std::min<uint64_t>(programs, ceil_div(total, slices));
+    uint64_t slices = 1, grid = 0;
+    if (part) {
+        // W equal sets of programs, one per destination, each walking all tiles
+        const uint64_t per_dest = std::min<uint64_t>(std::max<uint64_t>(programs / W, 1), total);
+        grid = per_dest * W;
+    } else {
+        // concurrent tiles per program: up to kCopyMaxSlices while every slice still gets a tile
+        while (!a2a && slices < static_cast<uint64_t>(kCopyMaxSlices) && programs * slices * 2 <= total) slices *= 2;
+        grid = std::min<uint64_t>(programs, ceil_div(total, slices));
+    }
+    if (grid >= (uint64_t{1} << 31)) return fail(AG_ERR_UNSUPPORTED, "n_programs too large");
+    const int vpt = static_cast<int>(tile_vecs / 256);
+    if (!ag::copy_supported(kind, vec, part ? 1 : W, p.dest_group, vpt))
+        return fail(AG_ERR_UNSUPPORTED, "no kernel for %d-byte vectors, %d destinations, group %d, %d vectors per thread",
+                    vec, part ? 1 : W, p.dest_group, vpt);
 
     p.vec_bytes = vec;
-    p.vectors_per_thread = static_cast<int32_t>(tile_vecs / 256);
+    p.vectors_per_thread = vpt;
     p.tiles_m = static_cast<int64_t>(tiles_m);
     p.tiles_n = static_cast<int64_t>(tiles_n);
     p.total_tiles = static_cast<int64_t>(total);
     p.n_programs = static_cast<int32_t>(grid);
     p.threads = static_cast<int32_t>(256 * slices);
+    p.variant = kind;
     *plan = p;
     return ok();
 }
 
-ag_status_t ag_all_gather(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
-                          const void* input, size_t out_offset, int64_t M_local, int64_t N,
-                          ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, void* stream)
+ag_status_t launch_copy_call(const ag_heap_t* heap, int kind, int W, int rank_start, int rank_stride,
+                             const void* input, size_t out_offset, int64_t M, int64_t N, ag_dtype_t dtype,
+                             int tile_m, int tile_n, int n_programs, const ag_copy_options_t* options, void* stream)
 {
     if (!heap) return fail(AG_ERR_INVALID_ARG, "heap is NULL");
     ag_heap_geometry_t geom;
     ag_heap_geometry(heap, &geom);
     ag_plan_t p;
-    ag_status_t s = ag_plan_all_gather(&geom, W, rank_start, rank_stride, reinterpret_cast<uint64_t>(input),
-                                       out_offset, M_local, N, dtype, tile_m, tile_n, n_programs, &p);
+    ag_status_t s = plan_copy(&geom, kind, W, rank_start, rank_stride, reinterpret_cast<uint64_t>(input), out_offset,
+                              M, N, dtype, tile_m, tile_n, n_programs, options, &p);
     if (s != AG_OK) return s;
     if (p.total_tiles == 0) return ok();
     const int e = elem_bytes(dtype);
+    const bool part = p.schedule == AG_SCHEDULE_PARTITIONED;
     ag::CopyLaunch l{};
     l.args.heap_bases = heap->core->table;
     l.args.input = static_cast<const uint8_t*>(input);
     l.args.rank_block_offset = p.rank_block_offset;
     l.args.row_bytes = static_cast<uint64_t>(N) * e;
-    l.args.rows = static_cast<uint32_t>(M_local);
+    l.args.chunk_bytes = static_cast<uint64_t>(M) * N * e;
+    l.args.rows = static_cast<uint32_t>(M);
     l.args.tile_m = static_cast<uint32_t>(p.tile_m);
     l.args.tile_row_bytes = static_cast<uint32_t>(p.tile_n) * e;
     l.args.vecs_per_row_log2 = static_cast<uint32_t>(log2_exact(static_cast<uint64_t>(p.tile_n) * e / p.vec_bytes));
@@ -427,13 +469,71 @@ ag_status_t ag_all_gather(const ag_heap_t* heap, int W, int rank_start, int rank
     l.args.rank_stride = rank_stride;
     l.args.group_rank = p.group_rank;
     l.args.slices = static_cast<uint32_t>(p.threads / 256);
+    l.args.world = static_cast<uint32_t>(W);
+    l.args.partitioned = part ? 1u : 0u;
+    l.kind = kind;
     l.vec_bytes = p.vec_bytes;
-    l.world = W;
+    l.dests = part ? 1 : W;
+    l.group = p.dest_group;
     l.vpt = p.vectors_per_thread;
     l.grid = p.n_programs;
     const hipError_t e2 = ag::launch_copy(l, static_cast<hipStream_t>(stream));
-    if (e2 != hipSuccess) return fail_hip(e2, "all-gather kernel launch");
+    if (e2 != hipSuccess) return fail_hip(e2, kind == ag::kCopyAllToAll ? "all-to-all kernel launch" : "all-gather kernel launch");
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+ag_status_t ag_plan_all_gather(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
+                               uint64_t input_addr, size_t out_offset, int64_t M_local, int64_t N,
+                               ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, ag_plan_t* plan)
+{
+    return plan_copy(geom, ag::kCopyAllGather, W, rank_start, rank_stride, input_addr, out_offset, M_local, N, dtype,
+                     tile_m, tile_n, n_programs, nullptr, plan);
+}
+
+ag_status_t ag_plan_all_gather_ex(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
+                                  uint64_t input_addr, size_t out_offset, int64_t M_local, int64_t N,
+                                  ag_dtype_t dtype, int tile_m, int tile_n, int n_programs,
+                                  const ag_copy_options_t* options, ag_plan_t* plan)
+{
+    return plan_copy(geom, ag::kCopyAllGather, W, rank_start, rank_stride, input_addr, out_offset, M_local, N, dtype,
+                     tile_m, tile_n, n_programs, options, plan);
+}
+
+ag_status_t ag_plan_all_to_all(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
+                               uint64_t input_addr, size_t out_offset, int64_t M_chunk, int64_t N,
+                               ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, ag_plan_t* plan)
+{
+    return plan_copy(geom, ag::kCopyAllToAll, W, rank_start, rank_stride, input_addr, out_offset, M_chunk, N, dtype,
+                     tile_m, tile_n, n_programs, nullptr, plan);
+}
+
+ag_status_t ag_all_gather(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                          const void* input, size_t out_offset, int64_t M_local, int64_t N,
+                          ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, void* stream)
+{
+    return launch_copy_call(heap, ag::kCopyAllGather, W, rank_start, rank_stride, input, out_offset, M_local, N,
+                            dtype, tile_m, tile_n, n_programs, nullptr, stream);
+}
+
+ag_status_t ag_all_gather_ex(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                             const void* input, size_t out_offset, int64_t M_local, int64_t N,
+                             ag_dtype_t dtype, int tile_m, int tile_n, int n_programs,
+                             const ag_copy_options_t* options, void* stream)
+{
+    return launch_copy_call(heap, ag::kCopyAllGather, W, rank_start, rank_stride, input, out_offset, M_local, N,
+                            dtype, tile_m, tile_n, n_programs, options, stream);
+}
+
+ag_status_t ag_all_to_all(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                          const void* input, size_t out_offset, int64_t M_chunk, int64_t N,
+                          ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, void* stream)
+{
+    return launch_copy_call(heap, ag::kCopyAllToAll, W, rank_start, rank_stride, input, out_offset, M_chunk, N,
+                            dtype, tile_m, tile_n, n_programs, nullptr, stream);
 }
 
 // ---------------------------------------------------------------------------

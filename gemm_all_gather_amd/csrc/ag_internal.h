@@ -7,13 +7,14 @@
 
 namespace ag {
 
-// Arguments of the persistent multi-destination copy kernel (by value).
+// Arguments of the persistent multi-destination copy kernels (by value).
 struct CopyKernelArgs {
     const uint64_t* heap_bases;   // device uint64_t[n_ranks]
-    const uint8_t* input;         // rank's M_local x N block, row-major
-    uint64_t rank_block_offset;   // out_offset + g*M_local*N*e, same in every region
+    const uint8_t* input;         // rank's M x N block (all-to-all: W such chunks), row-major
+    uint64_t rank_block_offset;   // out_offset + g*M*N*e, same in every region
     uint64_t row_bytes;           // N*e
-    uint32_t rows;                // M_local
+    uint64_t chunk_bytes;         // all-to-all: M*N*e between consecutive input chunks
+    uint32_t rows;                // M (M_local, or M_chunk for the all-to-all)
     uint32_t tile_m;              // rows per tile
     uint32_t tile_row_bytes;      // tile_n*e
     uint32_t vecs_per_row_log2;   // log2(tile_row_bytes / vec_bytes)
@@ -24,17 +25,25 @@ struct CopyKernelArgs {
     int32_t rank_stride;
     int32_t group_rank;           // g
     uint32_t slices;              // 256-thread slices per workgroup (blockDim.x / 256)
+    uint32_t world;               // group size W
+    uint32_t partitioned;         // 1: program p stores only to destination p % W (one destination per kernel)
     uint32_t reserved;
 };
 
+enum CopyKind { kCopyAllGather = 0, kCopyAllToAll = 1 };
+
 struct CopyLaunch {
     CopyKernelArgs args;
+    int kind;          // CopyKind
     int vec_bytes;     // 16, 8, 4, 2
-    int world;         // W
+    int dests;         // destinations each program stores a tile to (W, or 1 when partitioned)
+    int group;         // destinations per wait (0 = no waits between destinations)
     int vpt;           // vector accesses per thread per tile
     int grid;          // workgroups
 };
 
+// Whether the launcher has a kernel for (kind, vec, dests, group, vpt) (host-only).
+bool copy_supported(int kind, int vec_bytes, int dests, int group, int vpt);
 hipError_t launch_copy(const CopyLaunch& l, hipStream_t stream);
 
 // Arguments of the fused GEMM + multi-destination store kernel.

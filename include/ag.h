@@ -90,7 +90,24 @@ typedef struct ag_plan {
     uint64_t bytes_read;         /* algorithmic bytes read per call */
     uint64_t bytes_written;      /* algorithmic bytes written per call (W destinations) */
     double flops;                /* 2*M_local*N*K for the GEMM, 0 for the all-gather */
+    int32_t dest_group;          /* copy kernels: destinations stored per wait (0 = all of them, no wait) */
+    int32_t schedule;            /* copy kernels: ag_schedule_t of the launch */
 } ag_plan_t;
+
+/* Tile schedules of the all-gather. */
+typedef enum ag_schedule {
+    AG_SCHEDULE_TILES = 0,       /* each program walks tiles and stores every tile to all W destinations */
+    AG_SCHEDULE_PARTITIONED = 1  /* each program owns one destination and walks the tiles for it alone */
+} ag_schedule_t;
+
+/* Options of ag_all_gather_ex; all-zero (or a NULL pointer) is ag_all_gather. */
+typedef struct ag_copy_options {
+    int32_t dest_group;   /* 0: one straight run of W destination stores per tile (default).
+                             1, 2 or 4 (< W): store that many destinations, then wait until the
+                             stores before them have completed, then the next group */
+    int32_t schedule;     /* ag_schedule_t */
+    int32_t reserved[6];  /* must be 0 */
+} ag_copy_options_t;
 
 /* ------------------------------------------------------------------------
  * Symmetric heap (ROCm/iris #626 "Summary" and #591: one heap per rank,
@@ -181,6 +198,68 @@ ag_status_t ag_all_gather(const ag_heap_t* heap, int W, int rank_start, int rank
  * launching; fills *plan on AG_OK. */
 ag_status_t ag_plan_all_gather(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
                                uint64_t input_addr, size_t out_offset, int64_t M_local, int64_t N,
+                               ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, ag_plan_t* plan);
+
+/* ------------------------------------------------------------------------
+ * All-gather variants (ROCm/iris #594, "Reviewer performance evaluation"
+ * and "Compiler inspection and grouping"; ROCm/iris #591, "INLINE
+ * grouping"; ROCm/iris #626, "Triton CCL all-gather").  Same arguments,
+ * result and errors as ag_all_gather, plus:
+ *
+ * options->dest_group  peers stored per wait.  The pages leave open whether
+ *               keeping every destination's stores in flight at once costs
+ *               link efficiency; grouping stores G destinations, then waits
+ *               for the memory counter to retire everything before them.
+ *               Supported: 0 (no grouping), and 1, 2 or 4 when it is below
+ *               W and the vector width is 16 or 8 bytes (AG_ERR_UNSUPPORTED
+ *               otherwise).  G >= W is the same as 0.
+ * options->schedule    AG_SCHEDULE_PARTITIONED: the persistent programs are
+ *               split into W equal sets, set i storing only to destination
+ *               i of the rotated order (i = 0 is the local region); each
+ *               program walks its set's share of the tiles, so every input
+ *               tile is read W times (once per destination).  n_programs is
+ *               rounded down to a multiple of W (at least W); dest_group
+ *               must be 0.
+ * Plan: ag_plan_all_gather_ex reports dest_group and schedule as applied
+ * and bytes_read of the schedule (W times the input when partitioned).
+ * ------------------------------------------------------------------------ */
+ag_status_t ag_all_gather_ex(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                             const void* input, size_t out_offset, int64_t M_local, int64_t N,
+                             ag_dtype_t dtype, int tile_m, int tile_n, int n_programs,
+                             const ag_copy_options_t* options, void* stream);
+
+ag_status_t ag_plan_all_gather_ex(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
+                                  uint64_t input_addr, size_t out_offset, int64_t M_local, int64_t N,
+                                  ag_dtype_t dtype, int tile_m, int tile_n, int n_programs,
+                                  const ag_copy_options_t* options, ag_plan_t* plan);
+
+/* ------------------------------------------------------------------------
+ * All-to-all on the same heap and destination machinery (ROCm/iris #594,
+ * "Compiler inspection and grouping", and ROCm/iris #591, "Hoist the peer
+ * heap bases": the all_to_all collective has the same per-destination
+ * heap-base pattern).  The result is that of
+ * torch.distributed.all_to_all_single with equal splits:
+ *
+ * input         device, W chunks of M_chunk x N elements, row-major (ld = N),
+ *               chunk c at input + c*M_chunk*N*e; chunk c is destined for
+ *               group member c
+ * out_offset    byte offset (multiple of the element size) of the W*M_chunk x N
+ *               output inside every member region
+ * After the call completes, rows [g*M_chunk, (g+1)*M_chunk) of member j's
+ * output hold chunk j of this rank's input; no other byte of the slab
+ * changes.  Every destination base is translated once before the tile loop;
+ * for each tile the W chunks' tiles are loaded, then stored local region
+ * first and the peers in rotated order.  Tiles as for ag_all_gather (0,0 =
+ * 8x256), with at most 2 vector accesses per thread (AG_ERR_UNSUPPORTED
+ * otherwise).  M_chunk = 0 is a no-op.  input must not overlap any member's
+ * output block.
+ * ------------------------------------------------------------------------ */
+ag_status_t ag_all_to_all(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                          const void* input, size_t out_offset, int64_t M_chunk, int64_t N,
+                          ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, void* stream);
+
+ag_status_t ag_plan_all_to_all(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
+                               uint64_t input_addr, size_t out_offset, int64_t M_chunk, int64_t N,
                                ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, ag_plan_t* plan);
 
 /* ------------------------------------------------------------------------

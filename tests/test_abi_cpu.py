@@ -217,3 +217,105 @@ def test_heap_argument_validation_without_device():
     assert status_of(ag.Heap.wrap, 0, 2, MiB)[0] == ag.AG_ERR_INVALID_ARG
     assert status_of(ag.Heap.wrap, 1 << 30, 2, 1000)[0] == ag.AG_ERR_INVALID_ARG
     assert status_of(ag.Heap.wrap, (1 << 30) + 8, 2, MiB)[0] == ag.AG_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# all-gather variants: destination groups and the partitioned schedule
+# ---------------------------------------------------------------------------
+
+def plan_ex(g=None, W=8, inp=INPUT, off=0, M=1024, N=4096, dtype="f16", tm=0, tn=0, progs=0, group=0, sched=0):
+    return ag.plan_all_gather_ex(g or geom(), W, 0, 1, inp, off, M, N, dtype, tm, tn, progs, group, sched)
+
+
+def test_plan_ex_defaults_equal_plain_plan():
+    a, b = plan().as_dict(), plan_ex().as_dict()
+    assert a == b
+    assert a["dest_group"] == 0 and a["schedule"] == ag.AG_SCHEDULE_TILES
+
+
+@pytest.mark.parametrize("W,group,applied", [(8, 1, 1), (8, 2, 2), (8, 4, 4), (4, 4, 0), (2, 4, 0), (3, 2, 2),
+                                             (1, 1, 0)])
+def test_plan_destination_groups(W, group, applied):
+    p = plan_ex(g=geom(), W=W, group=group)
+    assert p.dest_group == applied
+    assert p.bytes_read == 1024 * 4096 * 2 and p.bytes_written == W * p.bytes_read   # grouping moves the same bytes
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(group=3), ag.AG_ERR_UNSUPPORTED),
+    (dict(group=8), ag.AG_ERR_UNSUPPORTED),
+    (dict(group=-1), ag.AG_ERR_INVALID_ARG),
+    (dict(group=2, sched=1), ag.AG_ERR_INVALID_ARG),
+    (dict(sched=2), ag.AG_ERR_INVALID_ARG),
+    (dict(group=2, M=64, N=4097, dtype="f32"), ag.AG_ERR_UNSUPPORTED),   # 4-byte vectors: no grouped kernel
+])
+def test_plan_ex_rejects(kw, status):
+    assert status_of(plan_ex, **kw)[0] == status
+
+
+def test_plan_ex_rejects_reserved_options():
+    o = ag._options(0, 0)
+    o.reserved[3] = 1
+    p = ag.Plan()
+    st = ag.lib().ag_plan_all_gather_ex(ctypes.byref(geom()), 8, 0, 1, INPUT, 0, 1024, 4096, ag.AG_F16, 0, 0, 0,
+                                        ctypes.byref(o), ctypes.byref(p))
+    assert st == ag.AG_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("W,progs,grid", [(8, 256, 256), (8, 100, 96), (8, 3, 8), (8, 0, 256), (3, 64, 63),
+                                          (1, 16, 16)])
+def test_plan_partitioned_programs(W, progs, grid):
+    p = plan_ex(g=geom(), W=W, progs=progs, sched="partitioned")
+    assert p.schedule == ag.AG_SCHEDULE_PARTITIONED
+    assert p.n_programs == grid and p.n_programs % W == 0 and p.threads == 256
+    blk = 1024 * 4096 * 2
+    assert p.bytes_read == W * blk and p.bytes_written == W * blk   # every destination reads the tile itself
+
+
+def test_plan_partitioned_programs_capped_by_tiles():
+    p = plan_ex(W=4, M=8, N=512, progs=256, sched="partitioned")   # 2 tiles of 8x256
+    assert p.total_tiles == 2 and p.n_programs == 2 * 4
+
+
+# ---------------------------------------------------------------------------
+# all-to-all
+# ---------------------------------------------------------------------------
+
+def plan_a2a(g=None, W=8, start=0, stride=1, inp=INPUT, off=0, M=128, N=4096, dtype="f16", tm=0, tn=0, progs=0):
+    return ag.plan_all_to_all(g or geom(), W, start, stride, inp, off, M, N, dtype, tm, tn, progs)
+
+
+def test_plan_all_to_all_default():
+    p = plan_a2a(g=geom(rank=5))
+    blk = 128 * 4096 * 2
+    assert p.group_rank == 5 and p.rank_block_offset == 5 * blk
+    assert p.bytes_read == 8 * blk and p.bytes_written == 8 * blk
+    assert (p.tile_m, p.tile_n, p.vec_bytes, p.vectors_per_thread) == (8, 256, 16, 1)
+    assert p.total_tiles == 16 * 16 and p.n_programs == 256 and p.threads == 256
+
+
+def test_plan_all_to_all_strided_group_and_zero_rows():
+    p = plan_a2a(g=geom(rank=5), W=4, start=1, stride=2, off=4096)
+    assert p.group_rank == 2 and p.rank_block_offset == 4096 + 2 * 128 * 4096 * 2
+    z = plan_a2a(M=0)
+    assert z.total_tiles == 0 and z.bytes_written == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tm=8, tn=512, dtype="f32"), ag.AG_ERR_UNSUPPORTED),     # 4 vectors per thread: at most 2
+    (dict(M=-1), ag.AG_ERR_INVALID_ARG),
+    (dict(M=1 << 20), ag.AG_ERR_INVALID_ARG),                     # output block past the region
+    (dict(inp=0), ag.AG_ERR_INVALID_ARG),
+    (dict(W=9), ag.AG_ERR_UNSUPPORTED),
+])
+def test_plan_all_to_all_rejects(kw, status):
+    assert status_of(plan_a2a, **kw)[0] == status
+
+
+def test_plan_all_to_all_input_may_not_overlap_any_output():
+    g = geom(rank=2)
+    blk = 128 * 4096 * 2
+    own = SLAB + 2 * g.bytes_per_rank + 2 * blk          # this rank's own rows: allowed for the all-gather only
+    assert status_of(plan_a2a, g=g, inp=own)[0] == ag.AG_ERR_INVALID_ARG
+    assert status_of(plan_a2a, g=g, inp=SLAB + 6 * g.bytes_per_rank + 8 * blk)[0] == ag.AG_OK   # past the block
+    assert status_of(plan_a2a, g=g, inp=SLAB + 6 * g.bytes_per_rank + 8 * blk - 2)[0] == ag.AG_ERR_INVALID_ARG

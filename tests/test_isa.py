@@ -83,7 +83,7 @@ COPY_CASES = [("16", "8", "1"), ("16", "8", "2"), ("8", "8", "2"), ("16", "4", "
 
 @pytest.mark.parametrize("vec,w,vpt", COPY_CASES)
 def test_copy_kernel_hoists_bases_and_never_drains_before_a_store(asm, vec, w, vpt):
-    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_copy_kernelILi{vec}ELi{w}ELi{vpt}E")
+    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_copy_kernelILi{vec}ELi{w}ELi{vpt}ELi0E")
     W, VPT = int(w), int(vpt)
     loops = _loops(lines)
     assert loops, "tile loop not found"
@@ -109,6 +109,41 @@ def test_copy_kernel_hoists_bases_and_never_drains_before_a_store(asm, vec, w, v
         assert not any(re.match(r"s_(cbranch|branch)", ln) for ln in body[first:last]), "destination loop back-edge"
     meta = _meta(asm["ag_copy.hip"], sym)
     assert meta["scratch"] == 0, meta
+
+
+@pytest.mark.parametrize("w,g", [(8, 1), (8, 2), (8, 4), (3, 2), (5, 4)])
+def test_grouped_copy_waits_once_per_destination_group(asm, w, g):
+    """dest_group G: after every G destinations' stores one wait retires what precedes them
+    (at most G stores stay in flight), and there is no other wait among the stores."""
+    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_copy_kernelILi16ELi{w}ELi1ELi{g}E")
+    h, b = _outermost(_loops(lines))
+    body = lines[h:b + 1]
+    stores = [i for i, ln in enumerate(body) if ln.startswith("buffer_store")]
+    assert len(stores) == 2 * w
+    for first, last in ((stores[0], stores[w - 1]), (stores[w], stores[-1])):
+        waits = [ln for ln in body[first:last] if ln.startswith("s_waitcnt")]
+        assert len(waits) == (w - 1) // g, waits
+        assert all(f"vmcnt({g})" in ln for ln in waits), waits
+    assert not any(ln.startswith("s_load") for ln in body)
+
+
+@pytest.mark.parametrize("w,vpt", [(8, 1), (8, 2), (4, 1), (2, 2)])
+def test_all_to_all_kernel_hoists_bases_and_pipelines_tiles(asm, w, vpt):
+    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_a2a_kernelILi16ELi{w}ELi{vpt}E")
+    loops = _loops(lines)
+    assert loops, "tile loop not found"
+    h, b = _outermost(loops)
+    body, prologue = lines[h:b + 1], lines[:h]
+    assert not any(ln.startswith("s_load") for ln in body), "scalar load inside the tile loop"
+    assert sum(ln.startswith("s_load_dwordx2") for ln in prologue) >= w
+    loads = [ln for ln in body if re.match(r"(buffer|global|flat)_load", ln)]
+    stores = [i for i, ln in enumerate(body) if ln.startswith("buffer_store")]
+    assert len(loads) == 2 * w * vpt and len(stores) == 2 * w * vpt   # two tiles per unrolled trip
+    prev = 0
+    for i in stores:
+        assert not [ln for ln in body[prev:i] if ln.startswith("s_waitcnt") and "vmcnt(0)" in ln]
+        prev = i
+    assert _meta(asm["ag_copy.hip"], sym)["scratch"] == 0
 
 
 @pytest.mark.parametrize("cfg", ["256ELi224", "256ELi256", "128ELi128"])
@@ -209,7 +244,7 @@ def test_fragment_hazard_check_catches_a_missing_wait():
 def test_report_registers(asm, capsys):
     """Print VGPR/AGPR/SGPR/scratch/LDS per instantiation (reported next to timings)."""
     rows = []
-    for src, pat in (("ag_copy.hip", r"ag_copy_kernel\S+"), ("ag_gemm.hip", r"ag_gemm_kernel\S+")):
+    for src, pat in (("ag_copy.hip", r"ag_(copy|a2a)_kernel\S+"), ("ag_gemm.hip", r"ag_gemm_kernel\S+")):
         for sym in re.findall(r"^\s*\.amdhsa_kernel (\S+)\s*$", asm[src], re.M):
             if re.search(pat, sym):
                 rows.append((sym, _meta(asm[src], sym)))
@@ -217,5 +252,5 @@ def test_report_registers(asm, capsys):
     with capsys.disabled():
         for sym, m in rows[:6] + rows[-6:]:
             print(f"{sym[:80]:80s} {m}")
-    # the copy kernels never spill
-    assert all(m["scratch"] == 0 for s, m in rows if "ag_copy_kernel" in s)
+    # the copy and all-to-all kernels never spill
+    assert all(m["scratch"] == 0 for s, m in rows if "ag_copy_kernel" in s or "ag_a2a_kernel" in s)
