@@ -112,6 +112,97 @@ def _cpu_baseline_fused(seconds: float):
                       f"(float64 numpy matmul + rounding), {reps * dt:.1f} s; BLAS may use up to {threads} threads"}
 
 
+def _context(args, stream, timed, views, ins, geom):
+    """Context measurements beside the headline (each job = the 8 ranks' calls, timed like it).
+
+    * the all-gather workload at the three program counts it is defined for;
+    * destination groups 1/2/4 and the partitioned schedule (all-gather variants);
+    * the all-to-all on the same heap: W=8, 8 chunks of 128x4096 fp16 per rank;
+    * the all-gather at 16384x8192 fp16 per rank (2.4 GB per call, steady state).
+    """
+    import torch
+    from gemm_all_gather_amd import binding as ag
+
+    steps = max(10, args.steps // 4)
+    sub = argparse.Namespace(**vars(args))
+    sub.steps, sub.warmup = steps, max(2, args.warmup // 2)
+    blk = AG_M * AG_N * 2
+    per_call = (1 + AG_W) * blk
+
+    def gbs(ms, bytes_per_call):
+        return round(AG_W * bytes_per_call / (ms / 1e3) / 1e9, 1)
+
+    ctx = {"steps": steps}
+    res = {}
+    for P in (64, 128, 256):
+        ms, _ = timed_sub(sub, timed, lambda P=P: [ag.all_gather(views[j], AG_W, 0, 1, ins[j], 0, AG_M, AG_N, AG_DTYPE,
+                                                                  *AG_TILE, P, stream) for j in range(AG_W)])
+        res[str(P)] = gbs(ms, per_call)
+    ctx["all_gather_GBs_by_programs"] = res
+    res = {}
+    for G in (1, 2, 4):
+        ms, _ = timed_sub(sub, timed, lambda G=G: [ag.all_gather_ex(views[j], AG_W, 0, 1, ins[j], 0, AG_M, AG_N,
+                                                                     AG_DTYPE, *AG_TILE, AG_PROGRAMS, G, 0, stream)
+                                                   for j in range(AG_W)])
+        res[str(G)] = gbs(ms, per_call)
+    ctx["all_gather_GBs_by_dest_group"] = res
+    res = {}
+    for P in (64, 128, 256):
+        ms, _ = timed_sub(sub, timed, lambda P=P: [ag.all_gather_ex(views[j], AG_W, 0, 1, ins[j], 0, AG_M, AG_N,
+                                                                     AG_DTYPE, *AG_TILE, P, 0, "partitioned", stream)
+                                                   for j in range(AG_W)])
+        # HBM bytes of the schedule: every destination reads the tile itself
+        res[str(P)] = gbs(ms, 2 * AG_W * blk)
+    ctx["partitioned_GBs_by_programs"] = res
+
+    # all-to-all: each rank sends 8 chunks of 128x4096 fp16 (8 MiB per rank, like the all-gather input)
+    mc = AG_M // AG_W
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    a2a_in = [torch.randint(-32768, 32767, (AG_W * mc * AG_N,), generator=g, dtype=torch.int16, device="cuda")
+              for _ in range(AG_W)]
+    a2a_plan = ag.plan_all_to_all(geom, AG_W, 0, 1, a2a_in[0], 0, mc, AG_N, AG_DTYPE, *AG_TILE, AG_PROGRAMS)
+    ms, _ = timed_sub(sub, timed, lambda: [ag.all_to_all(views[j], AG_W, 0, 1, a2a_in[j], 0, mc, AG_N, AG_DTYPE,
+                                                         *AG_TILE, AG_PROGRAMS, stream) for j in range(AG_W)])
+    a2a_bytes = a2a_plan.bytes_read + a2a_plan.bytes_written
+    launch_s = ms / 1e3 / AG_W
+    ctx["all_to_all"] = {
+        "workload": f"all-to-all W={AG_W}, {AG_W} chunks of {mc}x{AG_N} fp16 per rank, tile 8x256, "
+                    f"{a2a_plan.n_programs} programs (8 calls per job)",
+        "value": round(AG_W * a2a_bytes / (ms / 1e3) / 1e9, 1), "unit": "GB/s",
+        "roofline": {"bound": "hbm", "achieved": round(a2a_bytes / launch_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(a2a_bytes / launch_s / 1e9 / HBM_PEAK_GBS, 4),
+                     "alg_bytes_per_launch": a2a_bytes, "avg_launch_us": round(launch_s * 1e6, 3)},
+    }
+    del a2a_in
+
+    # the all-gather at 16384 x 8192 fp16 per rank: 2.4 GB per call
+    M3, N3 = 16384, 8192
+    blk3 = M3 * N3 * 2
+    S3 = AG_W * blk3
+    slab3 = torch.empty(AG_W * S3, dtype=torch.uint8, device="cuda")
+    heap3 = ag.Heap.wrap(slab3, AG_W, S3)
+    views3 = [heap3.view(r) for r in range(AG_W)]
+    g.manual_seed(6)
+    in3 = [torch.randint(-32768, 32767, (M3 * N3,), generator=g, dtype=torch.int16, device="cuda")
+           for _ in range(AG_W)]
+    sub3 = argparse.Namespace(**vars(sub))
+    sub3.steps, sub3.warmup = 5, 1
+    ms, _ = timed_sub(sub3, timed, lambda: [ag.all_gather(views3[j], AG_W, 0, 1, in3[j], 0, M3, N3, "f16", 8, 256,
+                                                          AG_PROGRAMS, stream) for j in range(AG_W)])
+    ctx["all_gather_16384x8192_fp16_GBs"] = round(AG_W * (1 + AG_W) * blk3 / (ms / 1e3) / 1e9, 1)
+    for v in views3:
+        v.destroy()
+    heap3.destroy()
+    del slab3, in3
+    torch.cuda.empty_cache()
+    return ctx
+
+
+def timed_sub(sub, timed, job):
+    return timed(job, sub)
+
+
 def main() -> int:
     global FU_M
     ap = argparse.ArgumentParser()
@@ -123,6 +214,9 @@ def main() -> int:
     ap.add_argument("--fused-m", type=int, default=FU_M, help="M_local of the fused workload (16384 or 1024)")
     ap.add_argument("--only", choices=["all", "copy", "fused"], default="all",
                     help="restrict the timed step to one kernel (profiling runs)")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context measurements (program counts, destination groups, partitioned "
+                         "schedule, all-to-all, 16384x8192 all-gather)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB "
                          "(reference for HBM byte counters)")
@@ -185,20 +279,20 @@ def main() -> int:
 
     # ---------------- warm-up and timed regions: the all-gather job K times, then the fused job K
     # times, each region bracketed by device synchronisation; a step is one of each
-    def timed(job):
-        for _ in range(args.warmup):
+    def timed(job, a=args):
+        for _ in range(a.warmup):
             job()
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for k in range(args.steps):
+        for k in range(a.steps):
             ev[k][0].record(stream)
             job()
             ev[k][1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return sum(a.elapsed_time(b) for a, b in ev) / args.steps, wall
+        return sum(x.elapsed_time(y) for x, y in ev) / a.steps, wall
 
     copy_ms, wall_copy = timed(copy_job) if args.only != "fused" else (0.0, 0.0)
     fused_ms, wall_fused = timed(fused_job) if (fused_ok and args.only != "copy") else (0.0, 0.0)
@@ -276,6 +370,8 @@ def main() -> int:
                                                        "total_tiles")},
         }
     out["copy_ms_per_job"] = round(copy_ms, 5)
+    if not args.no_context and args.only == "all":
+        out["context"] = _context(args, stream, timed, views, ins, geom)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline_copy(args.cpu_seconds)

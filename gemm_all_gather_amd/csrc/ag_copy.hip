@@ -5,7 +5,9 @@
 //   * before the tile loop, load the local heap base and every destination's
 //     heap base from the device table heap_bases once, and keep each
 //     destination as a 64-bit pointer delta (dest_base - local_base) in
-//     scalar registers;
+//     scalar registers (one vector load of the W entries, issued just ahead
+//     of the first two input tiles' loads so the latencies overlap, then
+//     readlane);
 //   * walk the tiles of the M_local x N input with a grid stride;
 //   * load each input tile once and store it to every destination: the
 //     local region first, then the peers in rotated group order
@@ -106,38 +108,16 @@ struct TileRef {
     uint32_t col0;       // byte column of the tile's first element
 };
 
-// Heap base of group member (g + i) mod world.
-__device__ inline uint64_t member_base(const CopyKernelArgs& a, int i)
-{
-    // g < world and i < 2*world: two conditional subtractions reduce mod world
-    int gi = a.group_rank + i;
-    if (gi >= static_cast<int>(a.world)) gi -= a.world;
-    if (gi >= static_cast<int>(a.world)) gi -= a.world;
-    return __builtin_nontemporal_load(a.heap_bases + (a.rank_start + gi * a.rank_stride));
-}
-
-// W destinations per tile (W = 1 when partitioned); G destinations per wait
-// (0: none).
-template <int VEC, int W, int VPT, int G>
+// W destinations per tile; G destinations per wait (0: none).  PART: the
+// partitioned schedule (W = 1, the group size is a.world at run time).
+template <int VEC, int W, int VPT, int G, bool PART>
 __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
 {
     using VT = Vec<VEC>;
     using V = typename VT::T;
     static_assert(G == 0 || G < W, "a group smaller than the destination count");
+    static_assert(!PART || (W == 1 && G == 0), "a partitioned program has one destination");
 
-    // ---- prologue: translate every destination once, before the tile loop.
-    // All table entries are requested before any is used, so the scalar
-    // loads overlap and the prologue pays one memory latency.  A partitioned
-    // program owns destination p % world of the rotated order.
-    const int first = a.partitioned ? static_cast<int>(blockIdx.x % a.world) : 0;
-    const uint64_t local_base = __builtin_nontemporal_load(a.heap_bases + a.rank);
-    uint64_t base[W];
-#pragma unroll
-    for (int i = 0; i < W; ++i) base[i] = member_base(a, first + i);
-    const uint64_t out_local = local_base + a.rank_block_offset;
-    uint64_t dest[W];   // out_local + (dest_base - local_base): local region first, then rotated peers
-#pragma unroll
-    for (int i = 0; i < W; ++i) dest[i] = out_local + static_cast<uint64_t>(static_cast<int64_t>(base[i] - local_base));
     const uint64_t input = reinterpret_cast<uint64_t>(a.input);
     const uint64_t block_bytes = static_cast<uint64_t>(a.rows) * a.row_bytes;
 
@@ -156,8 +136,8 @@ __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
     }
 
     // partitioned: the programs of one destination walk the tiles among themselves
-    const uint32_t stride = a.partitioned ? gridDim.x / a.world : gridDim.x * a.slices;
-    uint32_t t = a.partitioned ? blockIdx.x / a.world : blockIdx.x * a.slices + slice;
+    const uint32_t stride = PART ? gridDim.x / a.world : gridDim.x * a.slices;
+    uint32_t t = PART ? blockIdx.x / a.world : blockIdx.x * a.slices + slice;
     if (t >= a.total_tiles) return;
 
     // Tile -> (tm, tn), row-major over tiles.  Rows past M_local fall past the
@@ -184,6 +164,58 @@ __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
 #pragma unroll
         for (int j = 0; j < VPT; ++j) v[j] = VT::load(src, vo[j]);
     };
+
+    // ---- translate every destination once, before the tile loop.
+    // Destination i is group member (g + i) mod W (i = 0: the calling rank);
+    // a partitioned program owns destination p mod world of that order.  One
+    // vector load fetches every table entry (lane i: destination i, lane W:
+    // the local base); it is issued ahead of the first two tiles' loads, so
+    // the three latencies overlap and waiting for the table never waits for
+    // a tile; readlane then moves the entries to scalar registers.
+    const int world = PART ? static_cast<int>(a.world) : W;
+    const int first = PART ? static_cast<int>(blockIdx.x % a.world) : 0;
+    uint64_t table_entry;
+    {
+        const int l = static_cast<int>(threadIdx.x & 63u);
+        int entry = a.rank;
+        if (l < W) {
+            int gi = a.group_rank + first + l;   // < 2 * world
+            if (gi >= world) gi -= world;
+            entry = a.rank_start + gi * a.rank_stride;
+        }
+        table_entry = a.heap_bases[entry];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // the table load goes out first
+    // ---- the first two tiles
+    TileRef ta = origin(t, true), tb;
+    uint32_t oa[VPT], ob[VPT];
+    V va[VPT], vb[VPT];
+    offsets(ta, oa);
+    load_tile(ta, oa, va);
+    uint32_t tn = t + stride;
+    bool more = tn < a.total_tiles && tn > t;   // tn > t: no wrap-around
+    tb = origin(more ? tn : t, more);
+    offsets(tb, ob);
+    load_tile(tb, ob, vb);                      // prefetch (dropped when !more)
+
+    uint64_t base[W];
+    uint64_t local_base;
+    {
+        const uint64_t v = table_entry;
+        const uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+#pragma unroll
+        for (int i = 0; i <= W; ++i) {
+            const uint64_t b = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(hi, i))) << 32) |
+                               static_cast<uint32_t>(__builtin_amdgcn_readlane(lo, i));
+            if (i < W) base[i] = b;
+            else local_base = b;
+        }
+    }
+    const uint64_t out_local = local_base + a.rank_block_offset;
+    uint64_t dest[W];   // out_local + (dest_base - local_base): local region first, then rotated peers
+#pragma unroll
+    for (int i = 0; i < W; ++i) dest[i] = out_local + static_cast<uint64_t>(static_cast<int64_t>(base[i] - local_base));
+
     auto store_tile = [&](const TileRef& r, const uint32_t (&vo)[VPT], const V (&v)[VPT]) {
 #pragma unroll
         for (int i = 0; i < W; ++i) {   // local region first, then the rotated peers
@@ -201,17 +233,6 @@ __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
     // the first step is peeled so that the loop is always entered with the
     // same accesses in flight (one tile load issued before W*VPT stores) and
     // each wait covers only the prefetched loads, never the stores.
-    TileRef ta = origin(t, true), tb;
-    uint32_t oa[VPT], ob[VPT];
-    V va[VPT], vb[VPT];
-    offsets(ta, oa);
-    load_tile(ta, oa, va);
-
-    uint32_t tn = t + stride;
-    bool more = tn < a.total_tiles && tn > t;   // tn > t: no wrap-around
-    tb = origin(more ? tn : t, more);
-    offsets(tb, ob);
-    load_tile(tb, ob, vb);                      // prefetch (dropped when !more)
     store_tile(ta, oa, va);
     if (!more) return;
     t = tn;
@@ -246,15 +267,11 @@ __global__ __launch_bounds__(256) void ag_a2a_kernel(CopyKernelArgs a)
     using VT = Vec<VEC>;
     using V = typename VT::T;
 
-    const uint64_t local_base = __builtin_nontemporal_load(a.heap_bases + a.rank);
-    uint64_t dest[W];   // destination i = group member (g + i) mod W
-    uint64_t src[W];    // input chunk meant for destination i
+    uint64_t src[W];    // input chunk meant for destination i = group member (g + i) mod W
 #pragma unroll
     for (int i = 0; i < W; ++i) {
         int gi = a.group_rank + i;
         if (gi >= W) gi -= W;
-        const uint64_t b = __builtin_nontemporal_load(a.heap_bases + (a.rank_start + gi * a.rank_stride));
-        dest[i] = local_base + a.rank_block_offset + static_cast<uint64_t>(static_cast<int64_t>(b - local_base));
         src[i] = reinterpret_cast<uint64_t>(a.input) + static_cast<uint64_t>(gi) * a.chunk_bytes;
     }
     const uint64_t block_bytes = a.chunk_bytes;
@@ -296,14 +313,21 @@ __global__ __launch_bounds__(256) void ag_a2a_kernel(CopyKernelArgs a)
             for (int j = 0; j < VPT; ++j) v[i][j] = VT::load(s, vo[j]);
         }
     };
-    auto store_tile = [&](const TileRef& r, const uint32_t (&vo)[VPT], const V (&v)[W][VPT]) {
-#pragma unroll
-        for (int i = 0; i < W; ++i) {   // local region first, then the rotated peers
-            const __amdgpu_buffer_rsrc_t d = make_rsrc(dest[i] + r.off, r.records);
-#pragma unroll
-            for (int j = 0; j < VPT; ++j) VT::store(v[i][j], d, vo[j]);
+    // destination bases, once: one vector load of the table (lane i: member
+    // (g + i) mod W, lane W: the local base), issued ahead of the first two
+    // tiles' loads and moved to scalars by readlane
+    uint64_t table_entry;
+    {
+        const int l = static_cast<int>(threadIdx.x & 63u);
+        int entry = a.rank;
+        if (l < W) {
+            int gi = a.group_rank + l;
+            if (gi >= W) gi -= W;
+            entry = a.rank_start + gi * a.rank_stride;
         }
-    };
+        table_entry = a.heap_bases[entry];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // the table load goes out first
 
     // same two-register-set pipeline as the all-gather loop
     TileRef ta = origin(t, true), tb;
@@ -316,6 +340,27 @@ __global__ __launch_bounds__(256) void ag_a2a_kernel(CopyKernelArgs a)
     tb = origin(more ? tn : t, more);
     offsets(tb, ob);
     load_tile(tb, ob, vb);
+
+    uint64_t dest[W];
+    {
+        const uint32_t lo = static_cast<uint32_t>(table_entry), hi = static_cast<uint32_t>(table_entry >> 32);
+        const uint64_t local_base = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(hi, W))) << 32) |
+                                    static_cast<uint32_t>(__builtin_amdgcn_readlane(lo, W));
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            const uint64_t b = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(hi, i))) << 32) |
+                               static_cast<uint32_t>(__builtin_amdgcn_readlane(lo, i));
+            dest[i] = local_base + a.rank_block_offset + static_cast<uint64_t>(static_cast<int64_t>(b - local_base));
+        }
+    }
+    auto store_tile = [&](const TileRef& r, const uint32_t (&vo)[VPT], const V (&v)[W][VPT]) {
+#pragma unroll
+        for (int i = 0; i < W; ++i) {   // local region first, then the rotated peers
+            const __amdgpu_buffer_rsrc_t d = make_rsrc(dest[i] + r.off, r.records);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) VT::store(v[i][j], d, vo[j]);
+        }
+    };
     store_tile(ta, oa, va);
     if (!more) return;
     t = tn;
@@ -344,53 +389,61 @@ using CopyFn = void (*)(CopyKernelArgs);
 
 // ---- all-gather instantiations: VEC x W x VPT, destination groups G for
 // 16- and 8-byte vectors (G < W)
+// (the partitioned schedule: W = 1, G = 0, PART)
 template <int VEC, int W, int VPT>
-CopyFn pick_group(int g)
+CopyFn pick_group(int g, bool part)
 {
-    if (g == 0) return ag_copy_kernel<VEC, W, VPT, 0>;
+    if (part) {
+        if constexpr (W == 1) return g == 0 ? ag_copy_kernel<VEC, 1, VPT, 0, true> : nullptr;
+        return nullptr;
+    }
+    if (g == 0) return ag_copy_kernel<VEC, W, VPT, 0, false>;
     if constexpr (VEC >= 8) {
-        if constexpr (W > 1) if (g == 1) return ag_copy_kernel<VEC, W, VPT, 1>;
-        if constexpr (W > 2) if (g == 2) return ag_copy_kernel<VEC, W, VPT, 2>;
-        if constexpr (W > 4) if (g == 4) return ag_copy_kernel<VEC, W, VPT, 4>;
+        if constexpr (W > 1) if (g == 1) return ag_copy_kernel<VEC, W, VPT, 1, false>;
+        if constexpr (W > 2) if (g == 2) return ag_copy_kernel<VEC, W, VPT, 2, false>;
+        if constexpr (W > 4) if (g == 4) return ag_copy_kernel<VEC, W, VPT, 4, false>;
     }
     return nullptr;
 }
 
 template <int VEC, int W>
-CopyFn pick_vpt(int vpt, int g)
+CopyFn pick_vpt(int vpt, int g, bool part)
 {
     switch (vpt) {
-    case 1: return pick_group<VEC, W, 1>(g);
-    case 2: return pick_group<VEC, W, 2>(g);
-    case 4: return pick_group<VEC, W, 4>(g);
-    case 8: return pick_group<VEC, W, 8>(g);
+    case 1: return pick_group<VEC, W, 1>(g, part);
+    case 2: return pick_group<VEC, W, 2>(g, part);
+    case 4: return pick_group<VEC, W, 4>(g, part);
+    case 8: return pick_group<VEC, W, 8>(g, part);
     default: return nullptr;
     }
 }
 
 template <int VEC>
-CopyFn pick_world(int w, int vpt, int g)
+CopyFn pick_world(int w, int vpt, int g, bool part)
 {
     switch (w) {
-    case 1: return pick_vpt<VEC, 1>(vpt, g);
-    case 2: return pick_vpt<VEC, 2>(vpt, g);
-    case 3: return pick_vpt<VEC, 3>(vpt, g);
-    case 4: return pick_vpt<VEC, 4>(vpt, g);
-    case 5: return pick_vpt<VEC, 5>(vpt, g);
-    case 6: return pick_vpt<VEC, 6>(vpt, g);
-    case 7: return pick_vpt<VEC, 7>(vpt, g);
-    case 8: return pick_vpt<VEC, 8>(vpt, g);
+    case 1: return pick_vpt<VEC, 1>(vpt, g, part);
+    case 2: return pick_vpt<VEC, 2>(vpt, g, part);
+    case 3: return pick_vpt<VEC, 3>(vpt, g, part);
+    case 4: return pick_vpt<VEC, 4>(vpt, g, part);
+    case 5: return pick_vpt<VEC, 5>(vpt, g, part);
+    case 6: return pick_vpt<VEC, 6>(vpt, g, part);
+    case 7: return pick_vpt<VEC, 7>(vpt, g, part);
+    case 8: return pick_vpt<VEC, 8>(vpt, g, part);
     default: return nullptr;
     }
 }
 
-// ---- all-to-all instantiations: VEC x W x VPT (VPT <= 2)
+// ---- all-to-all instantiations: VEC x W x VPT with VEC*VPT <= 32 bytes per
+// thread and chunk tile (two register sets of W such tiles stay live)
 template <int VEC, int W>
 CopyFn pick_a2a_vpt(int vpt)
 {
     switch (vpt) {
     case 1: return ag_a2a_kernel<VEC, W, 1>;
     case 2: return ag_a2a_kernel<VEC, W, 2>;
+    case 4: if constexpr (VEC * 4 <= 32) return ag_a2a_kernel<VEC, W, 4>; else return nullptr;
+    case 8: if constexpr (VEC * 8 <= 32) return ag_a2a_kernel<VEC, W, 8>; else return nullptr;
     default: return nullptr;
     }
 }
@@ -411,7 +464,7 @@ CopyFn pick_a2a_world(int w, int vpt)
     }
 }
 
-CopyFn pick_kernel(int kind, int vec, int w, int g, int vpt)
+CopyFn pick_kernel(int kind, int vec, int w, int g, int vpt, bool part)
 {
     if (kind == kCopyAllToAll) {
         if (g != 0) return nullptr;
@@ -424,24 +477,24 @@ CopyFn pick_kernel(int kind, int vec, int w, int g, int vpt)
         }
     }
     switch (vec) {
-    case 16: return pick_world<16>(w, vpt, g);
-    case 8: return pick_world<8>(w, vpt, g);
-    case 4: return pick_world<4>(w, vpt, g);
-    case 2: return pick_world<2>(w, vpt, g);
+    case 16: return pick_world<16>(w, vpt, g, part);
+    case 8: return pick_world<8>(w, vpt, g, part);
+    case 4: return pick_world<4>(w, vpt, g, part);
+    case 2: return pick_world<2>(w, vpt, g, part);
     default: return nullptr;
     }
 }
 
 }  // namespace
 
-bool copy_supported(int kind, int vec_bytes, int dests, int group, int vpt)
+bool copy_supported(int kind, int vec_bytes, int dests, int group, int vpt, bool partitioned)
 {
-    return pick_kernel(kind, vec_bytes, dests, group, vpt) != nullptr;
+    return pick_kernel(kind, vec_bytes, dests, group, vpt, partitioned) != nullptr;
 }
 
 hipError_t launch_copy(const CopyLaunch& l, hipStream_t stream)
 {
-    CopyFn fn = pick_kernel(l.kind, l.vec_bytes, l.dests, l.group, l.vpt);
+    CopyFn fn = pick_kernel(l.kind, l.vec_bytes, l.dests, l.group, l.vpt, l.args.partitioned != 0);
     const uint32_t max_slices = l.kind == kCopyAllToAll ? 1 : 4;
     if (fn == nullptr || l.args.slices < 1 || l.args.slices > max_slices || l.grid < 1 || l.args.world < 1)
         return hipErrorInvalidValue;

@@ -395,7 +395,7 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     while (vec > e && ((row_bytes % vec) != 0 || (input_addr % vec) != 0 || (out_addr % vec) != 0)) vec /= 2;
     const uint64_t tile_row_bytes = static_cast<uint64_t>(tile_n) * e;
     const uint64_t tile_vecs = static_cast<uint64_t>(tile_m) * tile_row_bytes / vec;
-    const int max_vpt = a2a ? 2 : kCopyMaxVpt;
+    const int max_vpt = a2a ? std::min(32 / vec, kCopyMaxVpt) : kCopyMaxVpt;   // all-to-all: <= 32 bytes per thread
     if (tile_vecs % 256 != 0 || tile_vecs / 256 > static_cast<uint64_t>(max_vpt))
         return fail(AG_ERR_UNSUPPORTED, "tile %dx%d holds %llu %d-byte vectors; 256 to %d are supported",
                     tile_m, tile_n, static_cast<unsigned long long>(tile_vecs), vec, 256 * max_vpt);
@@ -422,7 +422,7 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     }
     if (grid >= (uint64_t{1} << 31)) return fail(AG_ERR_UNSUPPORTED, "n_programs too large");
     const int vpt = static_cast<int>(tile_vecs / 256);
-    if (!ag::copy_supported(kind, vec, part ? 1 : W, p.dest_group, vpt))
+    if (!ag::copy_supported(kind, vec, part ? 1 : W, p.dest_group, vpt, part))
         return fail(AG_ERR_UNSUPPORTED, "no kernel for %d-byte vectors, %d destinations, group %d, %d vectors per thread",
                     vec, part ? 1 : W, p.dest_group, vpt);
 

@@ -26,7 +26,7 @@ struct CopyKernelArgs {
     int32_t group_rank;           // g
     uint32_t slices;              // 256-thread slices per workgroup (blockDim.x / 256)
     uint32_t world;               // group size W
-    uint32_t partitioned;         // 1: program p stores only to destination p % W (one destination per kernel)
+    uint32_t partitioned;         // 1: program p stores only to destination p % W (the partitioned kernel)
     uint32_t reserved;
 };
 
@@ -42,8 +42,8 @@ struct CopyLaunch {
     int grid;          // workgroups
 };
 
-// Whether the launcher has a kernel for (kind, vec, dests, group, vpt) (host-only).
-bool copy_supported(int kind, int vec_bytes, int dests, int group, int vpt);
+// Whether the launcher has a kernel for (kind, vec, dests, group, vpt, schedule) (host-only).
+bool copy_supported(int kind, int vec_bytes, int dests, int group, int vpt, bool partitioned);
 hipError_t launch_copy(const CopyLaunch& l, hipStream_t stream);
 
 // Arguments of the fused GEMM + multi-destination store kernel.

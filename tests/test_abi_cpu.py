@@ -302,7 +302,7 @@ def test_plan_all_to_all_strided_group_and_zero_rows():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(tm=8, tn=512, dtype="f32"), ag.AG_ERR_UNSUPPORTED),     # 4 vectors per thread: at most 2
+    (dict(tm=8, tn=512, dtype="f32"), ag.AG_ERR_UNSUPPORTED),     # 64 bytes per thread: at most 32
     (dict(M=-1), ag.AG_ERR_INVALID_ARG),
     (dict(M=1 << 20), ag.AG_ERR_INVALID_ARG),                     # output block past the region
     (dict(inp=0), ag.AG_ERR_INVALID_ARG),
@@ -310,6 +310,12 @@ def test_plan_all_to_all_strided_group_and_zero_rows():
 ])
 def test_plan_all_to_all_rejects(kw, status):
     assert status_of(plan_a2a, **kw)[0] == status
+
+
+@pytest.mark.parametrize("N,vec,vpt", [(4096, 16, 1), (4092, 8, 2), (4094, 4, 4), (4095, 2, 8)])
+def test_plan_all_to_all_default_tile_fits_every_vector_width(N, vec, vpt):
+    p = plan_a2a(M=16, N=N)
+    assert (p.vec_bytes, p.vectors_per_thread) == (vec, vpt)
 
 
 def test_plan_all_to_all_input_may_not_overlap_any_output():

@@ -83,16 +83,26 @@ COPY_CASES = [("16", "8", "1"), ("16", "8", "2"), ("8", "8", "2"), ("16", "4", "
 
 @pytest.mark.parametrize("vec,w,vpt", COPY_CASES)
 def test_copy_kernel_hoists_bases_and_never_drains_before_a_store(asm, vec, w, vpt):
-    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_copy_kernelILi{vec}ELi{w}ELi{vpt}ELi0E")
+    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_copy_kernelILi{vec}ELi{w}ELi{vpt}ELi0ELb0E")
     W, VPT = int(w), int(vpt)
     loops = _loops(lines)
     assert loops, "tile loop not found"
     h, b = _outermost(loops)
     body = lines[h:b + 1]
     prologue = lines[:h]
-    # every heap-base (scalar) load happens before the tile loop
+    # the heap-base table is read once, before the tile loop: one vector load
+    # of the W entries (then readlane), issued just ahead of the first tiles'
     assert not any(ln.startswith("s_load") for ln in body), "scalar load inside the tile loop"
-    assert sum(ln.startswith("s_load_dwordx2") for ln in prologue) >= W
+    table = [i for i, ln in enumerate(prologue) if ln.startswith("global_load_dwordx2")]
+    assert len(table) == 1, table
+    assert sum(ln.startswith("v_readlane_b32") for ln in prologue) >= 2 * W
+    tiles = [i for i, ln in enumerate(prologue) if ln.startswith("buffer_load")]
+    assert len(tiles) == 2 * VPT and table[0] < tiles[0], "table, then the first two tiles"
+    # waiting for the table, then for the first tile, never waits for the prefetched second tile
+    first_store = next(i for i, ln in enumerate(prologue) if ln.startswith("buffer_store"))
+    counts = [int(re.search(r"vmcnt\((\d+)\)", ln).group(1)) for ln in prologue[tiles[-1]:first_store]
+              if ln.startswith("s_waitcnt") and "vmcnt" in ln]
+    assert counts and min(counts) >= VPT, counts
     # the only loads in the loop are the input tile's (two tiles per unrolled loop trip)
     loads = [ln for ln in body if re.match(r"(buffer|global|flat)_load", ln)]
     assert len(loads) == 2 * VPT, loads
@@ -115,7 +125,7 @@ def test_copy_kernel_hoists_bases_and_never_drains_before_a_store(asm, vec, w, v
 def test_grouped_copy_waits_once_per_destination_group(asm, w, g):
     """dest_group G: after every G destinations' stores one wait retires what precedes them
     (at most G stores stay in flight), and there is no other wait among the stores."""
-    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_copy_kernelILi16ELi{w}ELi1ELi{g}E")
+    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_copy_kernelILi16ELi{w}ELi1ELi{g}ELb0E")
     h, b = _outermost(_loops(lines))
     body = lines[h:b + 1]
     stores = [i for i, ln in enumerate(body) if ln.startswith("buffer_store")]
@@ -127,15 +137,16 @@ def test_grouped_copy_waits_once_per_destination_group(asm, w, g):
     assert not any(ln.startswith("s_load") for ln in body)
 
 
-@pytest.mark.parametrize("w,vpt", [(8, 1), (8, 2), (4, 1), (2, 2)])
-def test_all_to_all_kernel_hoists_bases_and_pipelines_tiles(asm, w, vpt):
-    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_a2a_kernelILi16ELi{w}ELi{vpt}E")
+@pytest.mark.parametrize("vec,w,vpt", [(16, 8, 1), (16, 8, 2), (16, 4, 1), (16, 2, 2), (8, 8, 4), (2, 3, 8)])
+def test_all_to_all_kernel_hoists_bases_and_pipelines_tiles(asm, vec, w, vpt):
+    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_a2a_kernelILi{vec}ELi{w}ELi{vpt}E")
     loops = _loops(lines)
     assert loops, "tile loop not found"
     h, b = _outermost(loops)
     body, prologue = lines[h:b + 1], lines[:h]
     assert not any(ln.startswith("s_load") for ln in body), "scalar load inside the tile loop"
-    assert sum(ln.startswith("s_load_dwordx2") for ln in prologue) >= w
+    assert sum(ln.startswith("global_load_dwordx2") for ln in prologue) == 1     # the table, once
+    assert sum(ln.startswith("v_readlane_b32") for ln in prologue) >= 2 * w
     loads = [ln for ln in body if re.match(r"(buffer|global|flat)_load", ln)]
     stores = [i for i, ln in enumerate(body) if ln.startswith("buffer_store")]
     assert len(loads) == 2 * w * vpt and len(stores) == 2 * w * vpt   # two tiles per unrolled trip
