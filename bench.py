@@ -2,7 +2,7 @@
 
 One step = one complete logical all-gather job on one GPU:
   * all-gather: every one of the W=8 logical ranks calls ag_all_gather on its
-    1024 x 4096 fp16 input (tile 8x256, 256 programs), so every heap region
+    1024 x 4096 fp16 input (tile 8x256, 128 programs), so every heap region
     ends up with the 8192 x 4096 gathered tensor;
   * fused: every one of the 8 logical ranks calls ag_gemm_all_gather with
     A_g 16384 x 8192 and the shared B 8192 x 3584 (fp16, fp32 accumulate),
@@ -34,8 +34,9 @@ METRIC = "all-gather achieved HBM GB/s (+% peak); fused GEMM+AG TFLOP/s (+% MFMA
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 
-# all-gather workload: W=8 logical ranks, 1024 x 4096 fp16 per rank
-AG_W, AG_M, AG_N, AG_DTYPE, AG_TILE, AG_PROGRAMS = 8, 1024, 4096, "f16", (8, 256), 256
+# all-gather workload: W=8 logical ranks, 1024 x 4096 fp16 per rank, tile 8x256; of the program
+# counts the workload is defined for (64/128/256, all three timed in "context"), 128
+AG_W, AG_M, AG_N, AG_DTYPE, AG_TILE, AG_PROGRAMS = 8, 1024, 4096, "f16", (8, 256), 128
 # fused workload: W=8, M_local 16384, K 8192, N 3584, fp16
 FU_W, FU_N, FU_K, FU_DTYPE = 8, 3584, 8192, "f16"
 FU_M = 16384
@@ -155,15 +156,15 @@ def _context(args, stream, timed, views, ins, geom):
         res[str(P)] = gbs(ms, 2 * AG_W * blk)
     ctx["partitioned_GBs_by_programs"] = res
 
-    # all-to-all: each rank sends 8 chunks of 128x4096 fp16 (8 MiB per rank, like the all-gather input)
-    mc = AG_M // AG_W
+    # all-to-all: each rank sends 8 chunks of 1024x4096 fp16 (64 MiB per rank)
+    mc = AG_M
     g = torch.Generator(device="cuda")
     g.manual_seed(5)
     a2a_in = [torch.randint(-32768, 32767, (AG_W * mc * AG_N,), generator=g, dtype=torch.int16, device="cuda")
               for _ in range(AG_W)]
-    a2a_plan = ag.plan_all_to_all(geom, AG_W, 0, 1, a2a_in[0], 0, mc, AG_N, AG_DTYPE, *AG_TILE, AG_PROGRAMS)
+    a2a_plan = ag.plan_all_to_all(geom, AG_W, 0, 1, a2a_in[0], 0, mc, AG_N, AG_DTYPE, *AG_TILE, 256)
     ms, _ = timed_sub(sub, timed, lambda: [ag.all_to_all(views[j], AG_W, 0, 1, a2a_in[j], 0, mc, AG_N, AG_DTYPE,
-                                                         *AG_TILE, AG_PROGRAMS, stream) for j in range(AG_W)])
+                                                         *AG_TILE, 256, stream) for j in range(AG_W)])
     a2a_bytes = a2a_plan.bytes_read + a2a_plan.bytes_written
     launch_s = ms / 1e3 / AG_W
     ctx["all_to_all"] = {
@@ -172,6 +173,7 @@ def _context(args, stream, timed, views, ins, geom):
         "value": round(AG_W * a2a_bytes / (ms / 1e3) / 1e9, 1), "unit": "GB/s",
         "roofline": {"bound": "hbm", "achieved": round(a2a_bytes / launch_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(a2a_bytes / launch_s / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic(f"ag_a2a_kernel_w{AG_W}_{mc}x{AG_N}_f16_pmc.md", "ag_copy.hip", a2a_bytes),
                      "alg_bytes_per_launch": a2a_bytes, "avg_launch_us": round(launch_s * 1e6, 3)},
     }
     del a2a_in
@@ -189,8 +191,8 @@ def _context(args, stream, timed, views, ins, geom):
     sub3 = argparse.Namespace(**vars(sub))
     sub3.steps, sub3.warmup = 5, 1
     ms, _ = timed_sub(sub3, timed, lambda: [ag.all_gather(views3[j], AG_W, 0, 1, in3[j], 0, M3, N3, "f16", 8, 256,
-                                                          AG_PROGRAMS, stream) for j in range(AG_W)])
-    ctx["all_gather_16384x8192_fp16_GBs"] = round(AG_W * (1 + AG_W) * blk3 / (ms / 1e3) / 1e9, 1)
+                                                          256, stream) for j in range(AG_W)])
+    ctx["all_gather_16384x8192_fp16_256_programs_GBs"] = round(AG_W * (1 + AG_W) * blk3 / (ms / 1e3) / 1e9, 1)
     for v in views3:
         v.destroy()
     heap3.destroy()
