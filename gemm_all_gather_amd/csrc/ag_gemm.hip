@@ -9,22 +9,28 @@
 // gfx950 design:
 //   * C = A . B with A row-major (M x K) and B K-contiguous (element (k,n) at
 //     B[n*ldb + k]); both operands are therefore rows of 128-byte K slabs.
-//   * 256 threads = 4 wave64s in a 2 x 2 grid; each wave owns a
-//     (TM/2) x (TN/2) sub-tile made of 16 x 16 blocks computed with
+//   * 8 wave64s (two per SIMD) in a 4 x 2 wave grid; each wave owns a
+//     (TM/4) x (TN/2) sub-tile made of 16 x 16 blocks computed with
 //     v_mfma_f32_16x16x32_{f16,bf16} into fp32 accumulators.
-//   * K advances 64 at a time through two LDS stages.  Each stage is filled
-//     by buffer_load_dwordx4 ... lds (global to LDS without VGPRs): one wave
+//   * K advances 64 at a time through a ring of LDS stages (two for the
+//     256-row tiles, four for 128 x 128).  Each stage is filled by
+//     buffer_load_dwordx4 ... lds (global to LDS without VGPRs): one wave
 //     instruction moves 8 rows x 128 bytes.  The 16-byte chunks of a row are
 //     XOR-swizzled by (row & 7), chosen through which global chunk each lane
 //     fetches, so the ds_read_b128 fragment reads are free of bank conflicts.
+//   * A wave that issues a stage's loads is held at each load until the CU
+//     accepts it.  With two ring slots the loads alternate between the two
+//     halves of the workgroup (stage k by half k % 2); waves are placed on
+//     SIMDs round-robin, so on every SIMD one wave keeps issuing MFMAs while
+//     the other issues loads.
 //   * The MFMA takes B as its first operand and A as its second, so each
 //     lane's accumulator holds four consecutive columns of one C row.
 //   * Epilogue: convert to the 16-bit output type (round to nearest even),
-//     stage the tile through LDS (reusing the two stages) so that every lane
-//     then holds 16 contiguous bytes of a C row, and store the tile to the W
-//     destinations with buffer_store_dwordx4: local region first, then the
-//     rotated peers.  Rows past M and columns past N are dropped by the
-//     buffer descriptors' bounds, never by branches.
+//     stage the tile through LDS (reusing the ring) so that every lane then
+//     holds 16 contiguous bytes of a C row, and store the tile to the W
+//     destinations with non-temporal buffer_store_dwordx4: local region
+//     first, then the rotated peers.  Rows past M and columns past N are
+//     dropped by the buffer descriptors' bounds, never by branches.
 //   * Tiles are walked by a persistent grid; consecutive workgroups land on
 //     different XCDs, so the tile order gives each XCD a compact group of
 //     tiles (8 tile rows at a time) that share A rows and B columns in its L2.
@@ -108,7 +114,7 @@ template <> struct Mfma<true> {
 // Tile configuration.  Named namespace: a kernel template instantiated with a
 // type of internal linkage gets no host-side launch handle.
 namespace gemm_cfg {
-template <int TM_, int TN_, int WGM_, int WGN_, int BK_, int NS_>
+template <int TM_, int TN_, int WGM_, int WGN_, int BK_, int NS_, bool ALT_>
 struct Cfg {
     static constexpr int TM = TM_, TN = TN_;
     static constexpr int WGM = WGM_, WGN = WGN_;           // wave grid
@@ -119,6 +125,7 @@ struct Cfg {
     static constexpr int BK = BK_;                         // K per LDS stage (32 or 64)
     static constexpr int KSUB = BK / 32;                   // MFMA K-steps (32 wide) per stage
     static constexpr int NS = NS_;                         // LDS ring slots
+    static constexpr bool ALT = ALT_;                      // stage loads by half the waves, alternating
     static constexpr int ROW_BYTES = BK * 2;               // bytes of one operand row in a stage
     static constexpr int LPR = ROW_BYTES / 16;             // lanes per row in a stage load
     static constexpr int RPI = 64 / LPR;                   // rows per 1-KiB wave load
@@ -144,6 +151,8 @@ struct Cfg {
     static_assert(QROWS % 16 == 0, "a 16-row accumulator block never straddles two staging slots");
     static_assert(A_INSTR % NW == 0, "every wave issues the same number of A loads");
     static_assert(BM + BN < 16, "one K-step's fragment reads fit the 4-bit LDS counter");
+    static_assert(!ALT || (NS == 2 && A_INSTR % (NW / 2) == 0 && B_INSTR % (NW / 2) == 0),
+                  "alternating loaders: two ring slots, an even split over half the waves");
     static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "gfx950 has 160 KiB of LDS");
 };
 }  // namespace gemm_cfg
@@ -188,6 +197,32 @@ struct Frag {
 // substitute in the host compilation pass.)
 template <class C>
 struct Stage {
+    // Alternating loaders: all A_INSTR + B_INSTR wave instructions of a stage
+    // are issued by one half of the workgroup's waves (wp = index within the
+    // half), instruction i = wp + (NW/2)*j of A, then of B.  la / lb are the
+    // lane's offsets inside a row group; the row group adds a uniform term.
+    static __device__ __forceinline__ void load_alt(uint64_t a_base, uint64_t a_records, uint64_t b_base,
+                                                    uint64_t b_records, uint8_t* slot, int kt, int wp, uint32_t la,
+                                                    uint32_t lb, uint32_t lda2, uint32_t ldb2)
+    {
+        constexpr int H = C::NW / 2;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, a_records);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, b_records);
+        const uint32_t soff = static_cast<uint32_t>(kt) * C::ROW_BYTES;
+#pragma unroll
+        for (int j = 0; j < C::A_INSTR / H; ++j) {
+            const int i = wp + H * j;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (AG_LDS void*)(slot + i * 1024), 16,
+                                                     la + static_cast<uint32_t>(i * C::RPI) * lda2, soff, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < C::B_INSTR / H; ++j) {
+            const int i = wp + H * j;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (AG_LDS void*)(slot + (C::A_INSTR + i) * 1024), 16,
+                                                     lb + static_cast<uint32_t>(i * C::RPI) * ldb2, soff, 0, 0);
+        }
+    }
+
     static __device__ __forceinline__ void load(uint64_t a_base, uint64_t a_records, uint64_t b_base,
                                                 uint64_t b_records, uint8_t* slot, int kt, int wave,
                                                 const uint32_t* voff)
@@ -241,6 +276,11 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
     const uint32_t ldb2 = static_cast<uint32_t>(a.ldb) * 2u;
     const uint32_t lrow = static_cast<uint32_t>(lane / C::LPR);                      // row in the load's row group
     const uint32_t lchunk = static_cast<uint32_t>(lane % C::LPR) ^ swz<C>(lrow);     // swizzled 16-byte chunk
+    const uint32_t la = lrow * lda2 + lchunk * 16u;
+    const uint32_t lb = lrow * ldb2 + lchunk * 16u;
+    // alternating loaders: waves are assigned to SIMDs round-robin, so each
+    // half has one wave on every SIMD
+    const int half = wave / (C::NW / 2), wp = wave % (C::NW / 2);
     uint32_t voff[C::MAXL];
 #pragma unroll
     for (int j = 0; j < C::MAXL; ++j) {
@@ -289,9 +329,19 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
             for (int bn = 0; bn < C::BN; ++bn) acc[bm][bn] = f32x4{0.f, 0.f, 0.f, 0.f};
         V fa[2][C::BM], fb[2][C::BN];
 
+        // Loads of stage kt into a ring slot.  With alternating loaders, half
+        // kt % 2 issues the whole stage: on every SIMD one wave is held up
+        // issuing loads while the other keeps the MFMA pipe busy.
         auto issue = [&](int slot, int kt) {
             const bool live = kt < kt_total;
-            Stage<C>::load(a_base, live ? a_records : 0, b_base, live ? b_records : 0, &ring[slot][0], kt, wave, voff);
+            if constexpr (C::ALT) {
+                if (half == (kt & 1))
+                    Stage<C>::load_alt(a_base, live ? a_records : 0, b_base, live ? b_records : 0, &ring[slot][0],
+                                       kt, wp, la, lb, lda2, ldb2);
+            } else {
+                Stage<C>::load(a_base, live ? a_records : 0, b_base, live ? b_records : 0, &ring[slot][0], kt, wave,
+                               voff);
+            }
         };
         // Fragment reads are inline assembly: the compiler cannot tell these
         // LDS reads apart from LDS-direct loads still landing in other ring
@@ -314,8 +364,16 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
         };
         auto wait_stages = [&](auto n_stages) {   // all of this wave's loads but the last n stages' have landed
             constexpr int n = decltype(n_stages)::value;
-            if (full_share) wait_vmcnt<n * C::MAXL>();
-            else wait_vmcnt<n * (C::MAXL - 1)>();
+            if constexpr (C::ALT) {
+                // two slots: a wave's only loads in flight at a boundary are
+                // those of the next stage, if it issued them (n == 0); in the
+                // prologue half 0 holds stage 0 and half 1 only stage 1
+                if (n == 0 || half == 0) wait_vmcnt<0>();
+            } else if (full_share) {
+                wait_vmcnt<n * C::MAXL>();
+            } else {
+                wait_vmcnt<n * (C::MAXL - 1)>();
+            }
         };
         // Stage s (in ring slot s % NS): its MFMA K-steps run on fragments read
         // one K-step ahead.  At the last K-step the next stage is made visible
@@ -431,18 +489,21 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
     }
 }
 
-// Instantiated configurations: tile, wave grid, K per stage, ring slots.
-// K = 64 per stage makes every operand row of a stage a full 128-byte line
-// (measured 1.7x the L2 -> LDS throughput of 64-byte rows), at the price of
-// only two ring slots for the 256-row tiles.
+// Instantiated configurations: tile, wave grid, K per stage, ring slots,
+// alternating loaders.  K = 64 per stage makes every operand row of a stage a
+// full 128-byte line (measured 1.7x the L2 -> LDS throughput of 64-byte
+// rows), at the price of only two ring slots for the 256-row tiles.
+// Alternating loaders measured 4% faster at 256 x 224; at 256 x 256 they
+// need a few more registers than the budget, so that tile keeps the loads
+// spread over all waves.
 #ifndef AG_GEMM_CFG_256x256
-#define AG_GEMM_CFG_256x256 256, 256, AG_GEMM_WGM, 2, 64, 2
+#define AG_GEMM_CFG_256x256 256, 256, AG_GEMM_WGM, 2, 64, 2, false
 #endif
 #ifndef AG_GEMM_CFG_256x224
-#define AG_GEMM_CFG_256x224 256, 224, AG_GEMM_WGM, 2, 64, 2
+#define AG_GEMM_CFG_256x224 256, 224, AG_GEMM_WGM, 2, 64, 2, true
 #endif
 #ifndef AG_GEMM_CFG_128x128
-#define AG_GEMM_CFG_128x128 128, 128, AG_GEMM_WGM, 2, 64, 4
+#define AG_GEMM_CFG_128x128 128, 128, AG_GEMM_WGM, 2, 64, 4, false
 #endif
 using CfgT256x256 = Cfg<AG_GEMM_CFG_256x256>;
 using CfgT256x224 = Cfg<AG_GEMM_CFG_256x224>;

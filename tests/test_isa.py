@@ -263,5 +263,5 @@ def test_report_registers(asm, capsys):
     with capsys.disabled():
         for sym, m in rows[:6] + rows[-6:]:
             print(f"{sym[:80]:80s} {m}")
-    # the copy and all-to-all kernels never spill
-    assert all(m["scratch"] == 0 for s, m in rows if "ag_copy_kernel" in s or "ag_a2a_kernel" in s)
+    # no kernel spills to scratch
+    assert all(m["scratch"] == 0 for s, m in rows), [s for s, m in rows if m["scratch"]][:3]
