@@ -19,10 +19,13 @@
 //     XOR-swizzled by (row & 7), chosen through which global chunk each lane
 //     fetches, so the ds_read_b128 fragment reads are free of bank conflicts.
 //   * A wave that issues a stage's loads is held at each load until the CU
-//     accepts it.  With two ring slots the loads alternate between the two
-//     halves of the workgroup (stage k by half k % 2); waves are placed on
-//     SIMDs round-robin, so on every SIMD one wave keeps issuing MFMAs while
-//     the other issues loads.
+//     accepts it (about one 1 KiB instruction per 22 cycles per CU).  With two
+//     ring slots the loads are split between the two halves of the
+//     workgroup and in time: stage k's A rows by half k % 2 right after the
+//     barrier two stages ahead, its B rows by the other half one stage
+//     ahead.  Waves are placed on SIMDs round-robin, so on every SIMD one
+//     wave keeps issuing MFMAs while the other issues loads.  Fragments are
+//     then single-buffered, which keeps the kernel within its registers.
 //   * The MFMA takes B as its first operand and A as its second, so each
 //     lane's accumulator holds four consecutive columns of one C row.
 //   * Epilogue: convert to the 16-bit output type (round to nearest even),
@@ -197,32 +200,36 @@ struct Frag {
 // substitute in the host compilation pass.)
 template <class C>
 struct Stage {
-    // Alternating loaders: all A_INSTR + B_INSTR wave instructions of a stage
-    // are issued by one half of the workgroup's waves (wp = index within the
-    // half), instruction i = wp + (NW/2)*j of A, then of B.  la / lb are the
-    // lane's offsets inside a row group; the row group adds a uniform term.
-    static __device__ __forceinline__ void load_alt(uint64_t a_base, uint64_t a_records, uint64_t b_base,
-                                                    uint64_t b_records, uint8_t* slot, int kt, int wp, uint32_t la,
-                                                    uint32_t lb, uint32_t lda2, uint32_t ldb2)
+    // Alternating loaders.  The stage's A_INSTR A-row and B_INSTR B-row wave
+    // instructions are issued by one half of the workgroup's waves (wp =
+    // index within the half): instruction i = wp + (NW/2)*j of each part.
+    // la / lb are the lane's offsets inside a row group; the row group adds
+    // a uniform term.  The operands are copied opaquely so that the
+    // per-instruction offsets are not hoisted into registers held across the
+    // K loop.
+    static __device__ __forceinline__ void load_part(bool a_part, uint64_t base, uint64_t records, uint8_t* slot,
+                                                     int kt, int wp, uint32_t lo, uint32_t ld2)
     {
         constexpr int H = C::NW / 2;
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, a_records);
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, b_records);
         const uint32_t soff = static_cast<uint32_t>(kt) * C::ROW_BYTES;
+        asm volatile("" : "+v"(lo), "+s"(ld2));
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base, records);
+        if (a_part) {
 #pragma unroll
-        for (int j = 0; j < C::A_INSTR / H; ++j) {
-            const int i = wp + H * j;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (AG_LDS void*)(slot + i * 1024), 16,
-                                                     la + static_cast<uint32_t>(i * C::RPI) * lda2, soff, 0, 0);
-        }
+            for (int j = 0; j < C::A_INSTR / H; ++j) {
+                const int i = wp + H * j;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (AG_LDS void*)(slot + i * 1024), 16,
+                                                         lo + static_cast<uint32_t>(i * C::RPI) * ld2, soff, 0, 0);
+            }
+        } else {
 #pragma unroll
-        for (int j = 0; j < C::B_INSTR / H; ++j) {
-            const int i = wp + H * j;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (AG_LDS void*)(slot + (C::A_INSTR + i) * 1024), 16,
-                                                     lb + static_cast<uint32_t>(i * C::RPI) * ldb2, soff, 0, 0);
+            for (int j = 0; j < C::B_INSTR / H; ++j) {
+                const int i = wp + H * j;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (AG_LDS void*)(slot + (C::A_INSTR + i) * 1024), 16,
+                                                         lo + static_cast<uint32_t>(i * C::RPI) * ld2, soff, 0, 0);
+            }
         }
     }
-
     static __device__ __forceinline__ void load(uint64_t a_base, uint64_t a_records, uint64_t b_base,
                                                 uint64_t b_records, uint8_t* slot, int kt, int wave,
                                                 const uint32_t* voff)
@@ -329,15 +336,15 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
             for (int bn = 0; bn < C::BN; ++bn) acc[bm][bn] = f32x4{0.f, 0.f, 0.f, 0.f};
         V fa[2][C::BM], fb[2][C::BN];
 
-        // Loads of stage kt into a ring slot.  With alternating loaders, half
-        // kt % 2 issues the whole stage: on every SIMD one wave is held up
-        // issuing loads while the other keeps the MFMA pipe busy.
+        // Loads of a whole stage kt into a ring slot (with alternating loaders:
+        // by half kt % 2; used for the first NS stages of a tile).
         auto issue = [&](int slot, int kt) {
             const bool live = kt < kt_total;
             if constexpr (C::ALT) {
-                if (half == (kt & 1))
-                    Stage<C>::load_alt(a_base, live ? a_records : 0, b_base, live ? b_records : 0, &ring[slot][0],
-                                       kt, wp, la, lb, lda2, ldb2);
+                if (half == (kt & 1)) {   // whole stage (prologue)
+                    Stage<C>::load_part(true, a_base, live ? a_records : 0, &ring[slot][0], kt, wp, la, lda2);
+                    Stage<C>::load_part(false, b_base, live ? b_records : 0, &ring[slot][0], kt, wp, lb, ldb2);
+                }
             } else {
                 Stage<C>::load(a_base, live ? a_records : 0, b_base, live ? b_records : 0, &ring[slot][0], kt, wave,
                                voff);
@@ -375,6 +382,38 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
                 wait_vmcnt<n * (C::MAXL - 1)>();
             }
         };
+        // Alternating loaders (two slots).  Stage s+2's A rows are loaded by
+        // half s % 2 right after the boundary barrier of stage s, into the
+        // slot stage s has just released; its B rows by the other half at the
+        // start of stage s+1.  Each wave is thus held at loads about half as
+        // long, at a different time from its SIMD partner, and at a boundary
+        // its only loads in flight are those of the next stage: vmcnt(0).
+        // Fragments are single-buffered: each K-step reads its own, waits,
+        // then issues its MFMAs (the SIMD partner hides the read latency).
+        auto stage_alt = [&](int s, int slot, int next_slot) {
+#pragma unroll
+            for (int kk = 0; kk < C::KSUB; ++kk) {
+                if (kk == 0 && s >= 1 && half != ((s - 1) & 1)) {
+                    const int kn = s + 1;
+                    Stage<C>::load_part(false, b_base, kn < kt_total ? b_records : 0, &ring[next_slot][0], kn, wp,
+                                        lb, ldb2);
+                }
+                read_frags(slot, kk, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_lgkmcnt0();
+                __builtin_amdgcn_sched_barrier(0);
+                if (kk + 1 == C::KSUB) {
+                    wait_vmcnt<0>();
+                    __builtin_amdgcn_s_barrier();
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int kn = s + C::NS;
+                    if (half == (kn & 1))
+                        Stage<C>::load_part(true, a_base, kn < kt_total ? a_records : 0, &ring[slot][0], kn, wp, la,
+                                            lda2);
+                }
+                mfmas(0);
+            }
+        };
         // Stage s (in ring slot s % NS): its MFMA K-steps run on fragments read
         // one K-step ahead.  At the last K-step the next stage is made visible
         // (its own loads waited for, then a barrier), the slot of stage s is
@@ -410,14 +449,16 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
         wait_stages(std::integral_constant<int, C::NS - 1>{});
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(0, 0, 0);
+        if constexpr (!C::ALT) read_frags(0, 0, 0);
 
         // ---- K loop, unrolled over the ring slots (and the fragment buffers)
         for (int s = 0; s < kt_total; s += C::UNROLL) {
 #pragma unroll
             for (int u = 0; u < C::UNROLL; ++u) {
-                if (u == 0 || s + u < kt_total)
-                    stage(s + u, u % C::NS, (u + 1) % C::NS, C::KSUB == 1 ? (u & 1) : 0);
+                if (u == 0 || s + u < kt_total) {
+                    if constexpr (C::ALT) stage_alt(s + u, u % C::NS, (u + 1) % C::NS);
+                    else stage(s + u, u % C::NS, (u + 1) % C::NS, C::KSUB == 1 ? (u & 1) : 0);
+                }
             }
         }
 
@@ -493,9 +534,9 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
 // alternating loaders.  K = 64 per stage makes every operand row of a stage a
 // full 128-byte line (measured 1.7x the L2 -> LDS throughput of 64-byte
 // rows), at the price of only two ring slots for the 256-row tiles.
-// Alternating loaders measured 4% faster at 256 x 224; at 256 x 256 they
-// need a few more registers than the budget, so that tile keeps the loads
-// spread over all waves.
+// Alternating loaders measured 5-7% faster at 256 x 224 (915 -> 850 us per
+// W=8 call at M_local 16384); the 256 x 256 tile keeps the loads spread over
+// all waves and double-buffered fragments.
 #ifndef AG_GEMM_CFG_256x256
 #define AG_GEMM_CFG_256x256 256, 256, AG_GEMM_WGM, 2, 64, 2, false
 #endif
