@@ -250,9 +250,9 @@ ag_status_t ag_plan_all_gather_ex(const ag_heap_geometry_t* geom, int W, int ran
  * changes.  Every destination base is translated once before the tile loop;
  * for each tile the W chunks' tiles are loaded, then stored local region
  * first and the peers in rotated order.  Tiles as for ag_all_gather (0,0 =
- * 8x256), with at most 2 vector accesses per thread (AG_ERR_UNSUPPORTED
- * otherwise).  M_chunk = 0 is a no-op.  input must not overlap any member's
- * output block.
+ * 8x256), holding at most 32 bytes per thread of a 256-thread workgroup
+ * (AG_ERR_UNSUPPORTED otherwise; 8x256 always fits).  M_chunk = 0 is a
+ * no-op.  input must not overlap any member's output block.
  * ------------------------------------------------------------------------ */
 ag_status_t ag_all_to_all(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
                           const void* input, size_t out_offset, int64_t M_chunk, int64_t N,
