@@ -118,8 +118,10 @@ def _context(args, stream, timed, views, ins, geom):
 
     * the all-gather workload at the three program counts it is defined for;
     * destination groups 1/2/4 and the partitioned schedule (all-gather variants);
-    * the all-to-all on the same heap: W=8, 8 chunks of 128x4096 fp16 per rank;
-    * the all-gather at 16384x8192 fp16 per rank (2.4 GB per call, steady state).
+    * the all-to-all on the same heap: W=8, 8 chunks of 1024x4096 fp16 per rank;
+    * the all-gather at 16384x8192 per rank in fp16, bf16 and fp32 (2.4 / 2.4 / 4.8 GB per call);
+    * the edge shapes: 1000x4100 fp16 (8-byte vectors, partial last column tile) at W=8, and the
+      strided group of ranks 1, 3, 5, 7 (W=4) at 1000x4100 and 16384x8192.
     """
     import torch
     from gemm_all_gather_amd import binding as ag
@@ -178,27 +180,97 @@ def _context(args, stream, timed, views, ins, geom):
     }
     del a2a_in
 
-    # the all-gather at 16384 x 8192 fp16 per rank: 2.4 GB per call
-    M3, N3 = 16384, 8192
-    blk3 = M3 * N3 * 2
-    S3 = AG_W * blk3
-    slab3 = torch.empty(AG_W * S3, dtype=torch.uint8, device="cuda")
-    heap3 = ag.Heap.wrap(slab3, AG_W, S3)
-    views3 = [heap3.view(r) for r in range(AG_W)]
-    g.manual_seed(6)
-    in3 = [torch.randint(-32768, 32767, (M3 * N3,), generator=g, dtype=torch.int16, device="cuda")
-           for _ in range(AG_W)]
     sub3 = argparse.Namespace(**vars(sub))
     sub3.steps, sub3.warmup = 5, 1
-    ms, _ = timed_sub(sub3, timed, lambda: [ag.all_gather(views3[j], AG_W, 0, 1, in3[j], 0, M3, N3, "f16", 8, 256,
-                                                          256, stream) for j in range(AG_W)])
-    ctx["all_gather_16384x8192_fp16_256_programs_GBs"] = round(AG_W * (1 + AG_W) * blk3 / (ms / 1e3) / 1e9, 1)
-    for v in views3:
-        v.destroy()
-    heap3.destroy()
-    del slab3, in3
-    torch.cuda.empty_cache()
+
+    def gather_rate(M3, N3, dtype, W3, start, stride, programs, seed):
+        """GB/s of one group's all-gather job ((1+W)*M*N*e per call) on a fresh 8-region heap."""
+        e3 = 4 if dtype == "f32" else 2
+        blk3 = M3 * N3 * e3
+        S3 = ((8 * blk3) // (2 << 20) + 1) * (2 << 20)
+        slab3 = torch.empty(8 * S3, dtype=torch.uint8, device="cuda")
+        heap3 = ag.Heap.wrap(slab3, 8, S3)
+        views3 = [heap3.view(r) for r in range(8)]
+        members = [start + i * stride for i in range(W3)]
+        g.manual_seed(seed)
+        in3 = [torch.randint(-32768, 32767, (blk3 // 2,), generator=g, dtype=torch.int16, device="cuda")
+               for _ in members]
+        ms, _ = timed_sub(sub3, timed, lambda: [ag.all_gather(views3[r], W3, start, stride, in3[i], 0, M3, N3,
+                                                              dtype, 0, 0, programs, stream)
+                                                for i, r in enumerate(members)])
+        for v in views3:
+            v.destroy()
+        heap3.destroy()
+        del slab3, in3
+        torch.cuda.empty_cache()
+        return round(W3 * (1 + W3) * blk3 / (ms / 1e3) / 1e9, 1)
+
+    # the all-gather at 16384 x 8192 per rank (2.4 GB per call in 16 bits), three element types
+    ctx["all_gather_16384x8192_256_programs_GBs_by_dtype"] = {
+        dt: gather_rate(16384, 8192, dt, AG_W, 0, 1, 256, 6) for dt in ("f16", "bf16", "f32")}
+    # the edge shapes: rows of 4100 elements (8-byte vectors, partial last column tile); the strided
+    # group of ranks 1, 3, 5, 7 (W=4) at both sizes
+    ctx["all_gather_edges_GBs"] = {
+        "1000x4100_f16_W8": gather_rate(1000, 4100, "f16", AG_W, 0, 1, 256, 7),
+        "1000x4100_f16_W4_group_1_2": gather_rate(1000, 4100, "f16", 4, 1, 2, 256, 8),
+        "16384x8192_f16_W4_group_1_2": gather_rate(16384, 8192, "f16", 4, 1, 2, 256, 9),
+    }
     return ctx
+
+
+def _context_fused(args, stream, timed, views, fu_off):
+    """The fused workload at M_local 1024 (fp16) and at M_local 16384 in bf16, W=8, timed like the headline."""
+    import numpy as np
+    import torch
+    from gemm_all_gather_amd import binding as ag
+    from gemm_all_gather_amd import inputs as gen
+
+    sub = argparse.Namespace(**vars(args))
+    sub.steps, sub.warmup = max(5, args.steps // 10), 2
+    res = {}
+    region = views[0].geometry().bytes_per_rank
+    for name, M, dtype in (("M1024_f16", 1024, "f16"), ("M16384_bf16", 16384, "bf16")):
+        if fu_off + FU_W * M * FU_N * 2 > region:   # heap sized for a smaller --fused-m
+            continue
+        fa = [torch.from_numpy(gen.normal_scaled((M, FU_K), dtype, FU_K ** -0.5, 12, j).view(np.uint8)
+                               .reshape(-1).copy()).cuda() for j in range(FU_W)]
+        fb = torch.from_numpy(gen.normal_scaled((FU_N, FU_K), dtype, FU_K ** -0.5, 13).view(np.uint8)
+                              .reshape(-1).copy()).cuda()
+        ms, _ = timed(lambda: [ag.gemm_all_gather(views[j], FU_W, 0, 1, fa[j], FU_K, fb, FU_K, fu_off, M, FU_N, FU_K,
+                                                  dtype, 0, 0, 0, 0, stream) for j in range(FU_W)], sub)
+        flops = 2.0 * M * FU_N * FU_K
+        tf = FU_W * flops / (ms / 1e3) / 1e12
+        res[name] = {"TFLOPs": round(tf, 1), "frac_of_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                     "us_per_call": round(ms * 1e3 / FU_W, 1)}
+        del fa, fb
+        torch.cuda.empty_cache()
+    return res
+
+
+def _calibration(stream):
+    """Plain device copy and fill of 2 GiB: what the part reaches on a pure stream (context only)."""
+    import torch
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    out = {}
+    for name, fn, nbytes in (("copy_2GiB_GBs", lambda: dst.copy_(src), 2 * n), ("fill_2GiB_GBs", lambda: dst.fill_(3), n)):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        ts.sort()
+        out[name] = round(nbytes / ts[len(ts) // 2] / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
 
 
 def timed_sub(sub, timed, job):
@@ -218,7 +290,8 @@ def main() -> int:
                     help="restrict the timed step to one kernel (profiling runs)")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context measurements (program counts, destination groups, partitioned "
-                         "schedule, all-to-all, 16384x8192 all-gather)")
+                         "schedule, all-to-all, 16384x8192 all-gather in three types, edge shapes, the fused "
+                         "workload at M_local 1024 and in bf16, plain copy/fill calibration)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB "
                          "(reference for HBM byte counters)")
@@ -281,6 +354,8 @@ def main() -> int:
 
     # ---------------- warm-up and timed regions: the all-gather job K times, then the fused job K
     # times, each region bracketed by device synchronisation; a step is one of each
+    spread = {}
+
     def timed(job, a=args):
         for _ in range(a.warmup):
             job()
@@ -294,7 +369,10 @@ def main() -> int:
             ev[k][1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return sum(x.elapsed_time(y) for x, y in ev) / a.steps, wall
+        per = sorted(x.elapsed_time(y) for x, y in ev)
+        spread[id(job)] = {"step_ms_median": round(per[len(per) // 2], 5), "step_ms_min": round(per[0], 5),
+                           "step_ms_max": round(per[-1], 5)}
+        return sum(per) / a.steps, wall
 
     copy_ms, wall_copy = timed(copy_job) if args.only != "fused" else (0.0, 0.0)
     fused_ms, wall_fused = timed(fused_job) if (fused_ok and args.only != "copy") else (0.0, 0.0)
@@ -343,6 +421,7 @@ def main() -> int:
             "alg_bytes_per_launch": per_call_bytes,
             "avg_launch_us": round(copy_launch_s * 1e6, 3),
         },
+        "spread": spread.get(id(copy_job)),
         "device": {"name": dev_props.name, "cus": dev_props.multi_processor_count},
         "plan_all_gather": {k: ag_plan.as_dict()[k] for k in ("vec_bytes", "n_programs", "threads", "total_tiles",
                                                               "vectors_per_thread")},
@@ -370,10 +449,13 @@ def main() -> int:
             },
             "plan": {k: fu_plan.as_dict()[k] for k in ("tile_m", "tile_n", "tile_k", "n_programs", "threads",
                                                        "total_tiles")},
+            "spread": spread.get(id(fused_job)),
         }
     out["copy_ms_per_job"] = round(copy_ms, 5)
     if not args.no_context and args.only == "all":
         out["context"] = _context(args, stream, timed, views, ins, geom)
+        out["context"]["fused"] = _context_fused(args, stream, timed, views, fu_off)
+        out["context"]["calibration"] = _calibration(stream)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline_copy(args.cpu_seconds)
