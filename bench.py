@@ -315,10 +315,8 @@ def main() -> int:
     # ---------------- all-gather setup
     e = 2
     blk = AG_M * AG_N * e
-    S_ag = AG_W * blk
-    # fused output block lives after the all-gather output in the same heap
-    fblk = FU_M * FU_N * 2
-    S = ((S_ag + FU_W * fblk) // (2 << 20) + 1) * (2 << 20)
+    # each workload has a heap of its own, every region sized for its gathered output (2 MiB multiples)
+    S = -(-(AG_W * blk) // (2 << 20)) * (2 << 20)
     slab = torch.empty(AG_W * S, dtype=torch.uint8, device="cuda")
     slab.zero_()
     heap = ag.Heap.wrap(slab, AG_W, S)
@@ -341,16 +339,23 @@ def main() -> int:
                            .reshape(-1).copy()).cuda() for j in range(FU_W)]
     fb = torch.from_numpy(gen.normal_scaled((FU_N, FU_K), FU_DTYPE, FU_K ** -0.5, 3).view(np.uint8)
                           .reshape(-1).copy()).cuda()
-    fu_off = S_ag
+    fblk = FU_M * FU_N * 2
+    SF = -(-(FU_W * fblk) // (2 << 20)) * (2 << 20)
+    fslab = torch.empty(FU_W * SF, dtype=torch.uint8, device="cuda")
+    fslab.zero_()
+    fheap = ag.Heap.wrap(fslab, FU_W, SF)
+    fviews = [fheap.view(r) for r in range(FU_W)]
+    fu_off = 0
 
     def fused_job():
         if args.only == "copy":
             return
         for j in range(FU_W):
-            ag.gemm_all_gather(views[j], FU_W, 0, 1, fa[j], FU_K, fb, FU_K, fu_off, FU_M, FU_N, FU_K, FU_DTYPE,
+            ag.gemm_all_gather(fviews[j], FU_W, 0, 1, fa[j], FU_K, fb, FU_K, fu_off, FU_M, FU_N, FU_K, FU_DTYPE,
                                0, 0, 0, 0, stream)
 
-    fu_plan = ag.plan_gemm_all_gather(geom, FU_W, 0, 1, fa[0], FU_K, fb, FU_K, fu_off, FU_M, FU_N, FU_K, FU_DTYPE)
+    fu_plan = ag.plan_gemm_all_gather(fviews[0].geometry(), FU_W, 0, 1, fa[0], FU_K, fb, FU_K, fu_off, FU_M, FU_N,
+                                      FU_K, FU_DTYPE)
 
     # ---------------- warm-up and timed regions: the all-gather job K times, then the fused job K
     # times, each region bracketed by device synchronisation; a step is one of each
@@ -454,7 +459,7 @@ def main() -> int:
     out["copy_ms_per_job"] = round(copy_ms, 5)
     if not args.no_context and args.only == "all":
         out["context"] = _context(args, stream, timed, views, ins, geom)
-        out["context"]["fused"] = _context_fused(args, stream, timed, views, fu_off)
+        out["context"]["fused"] = _context_fused(args, stream, timed, fviews, fu_off)
         out["context"]["calibration"] = _calibration(stream)
 
     if not args.no_cpu_baseline:
@@ -462,9 +467,10 @@ def main() -> int:
         if fused_ok:
             out["fused"]["cpu_baseline"] = _cpu_baseline_fused(args.cpu_seconds)
     print(json.dumps(out), flush=True)
-    for v in views:
+    for v in views + fviews:
         v.destroy()
     heap.destroy()
+    fheap.destroy()
     return 0
 
 
