@@ -260,8 +260,19 @@ def test_report_registers(asm, capsys):
             if re.search(pat, sym):
                 rows.append((sym, _meta(asm[src], sym)))
     assert rows
+    # the instantiations the benchmark workloads run, then a summary over all of them
+    bench = [r"ag_copy_kernelILi16ELi8ELi1ELi0ELb0E", r"ag_a2a_kernelILi16ELi8ELi1E",
+             r"ag_gemm_kernelILb0ELi8E\S*CfgILi256ELi224E", r"ag_gemm_kernelILb1ELi8E\S*CfgILi256ELi224E",
+             r"ag_gemm_kernelILb0ELi8E\S*CfgILi128ELi128E", r"ag_gemm_kernelILb0ELi1E\S*CfgILi256ELi224E"]
     with capsys.disabled():
-        for sym, m in rows[:6] + rows[-6:]:
-            print(f"{sym[:80]:80s} {m}")
+        print()
+        for pat in bench:
+            for sym, m in rows:
+                if re.search(pat, sym):
+                    print(f"{sym[:100]:100s} vgpr={m['vgpr']} agpr_offset={m['agpr_offset']} sgpr={m['sgpr']} "
+                          f"scratch={m['scratch']} lds={m['lds']}")
+                    break
+        print(f"{len(rows)} instantiations: max vgpr {max(m['vgpr'] for _, m in rows)}, "
+              f"max sgpr {max(m['sgpr'] for _, m in rows)}, total scratch {sum(m['scratch'] for _, m in rows)}")
     # no kernel spills to scratch
     assert all(m["scratch"] == 0 for s, m in rows), [s for s, m in rows if m["scratch"]][:3]
