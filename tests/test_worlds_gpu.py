@@ -1,10 +1,12 @@
-"""Parity at the group sizes the other sweeps leave out: W = 5, 6 and 7.
+"""Parity at the group sizes the other sweeps leave out (W = 5, 6 and 7), and
+the fused kernel on small persistent grids.
 
 The kernels unroll the destination loop for every W in 1..8; these cases run
 the plain all-gather, the all-to-all and the fused GEMM + all-gather at the
-three odd-sized groups, contiguous and strided, each against the oracle over
-the whole heap (bit-exact; the fused case uses small-integer operands, whose
-products and sums are exact).
+three odd-sized groups, contiguous and offset, each against the oracle over
+the whole heap (bit-exact; the fused cases use small-integer operands, whose
+products and sums are exact).  The last test gives the fused kernel 1 to 24
+programs for a ragged 600 x 464 output, so every program walks many tiles.
 """
 
 import numpy as np
@@ -60,6 +62,33 @@ def test_fused_odd_worlds_bit_exact(W, start, stride, dtype):
         before = th.host()
         _run_fused(th, [to_device(x) for x in a], [to_device(x) for x in b], W, start, stride, off, M, N, K,
                    dtype, tile)
+        got = th.host()
+        want = gemm_all_gather_oracle(before, S, a, b, dtype, start, stride, off)
+        if not np.array_equal(got, want):
+            bad = np.flatnonzero(got != want)
+            raise AssertionError(f"{bad.size} bytes differ, first at region {bad[0] // S} offset {bad[0] % S}")
+    finally:
+        th.close()
+
+
+@pytest.mark.parametrize("programs", [1, 3, 8, 24])
+@pytest.mark.parametrize("tile", [(256, 224, 64), (256, 256, 64), (128, 128, 64)])
+def test_fused_few_programs_many_tiles_bit_exact(programs, tile):
+    """Small persistent grids: every program walks many tiles (ragged in M and N), with and without the
+    XCD renumbering of the tile order (program counts that are, or are not, multiples of 8)."""
+    require_gpu()
+    M, N, K, dtype = 600, 464, 256, "f16"
+    W, start, stride = 4, 1, 2
+    off = 4096
+    log(f"fused int M={M} N={N} K={K} tile={tile} programs={programs} W={W} group=({start},{stride})")
+    a = [gen.small_integers((M, K), dtype, -3, 3, 7, programs, j) for j in range(W)]
+    b = [gen.small_integers((N, K), dtype, -3, 3, 8, programs, j) for j in range(W)]
+    S = _region_size(W, M, N, off)
+    th = TorchHeap(8, S)
+    try:
+        before = th.host()
+        _run_fused(th, [to_device(x) for x in a], [to_device(x) for x in b], W, start, stride, off, M, N, K,
+                   dtype, tile, programs)
         got = th.host()
         want = gemm_all_gather_oracle(before, S, a, b, dtype, start, stride, off)
         if not np.array_equal(got, want):
