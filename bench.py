@@ -284,7 +284,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-m", type=int, default=FU_M, help="M_local of the fused workload (16384 or 1024)")
@@ -363,26 +363,41 @@ def main() -> int:
     # times, each region bracketed by device synchronisation; a step is one of each
     spread = {}
 
-    def timed(job, a=args):
+    # K steps between one pair of HIP events, bracketed by device synchronisation.  (An event pair
+    # around every step measured ~2% slower on the all-gather job: the kernel after each event
+    # record starts later.)  With blocks > 0, that many further runs of up to 20 steps, each with
+    # its own event pair, give the spread of the per-step time.
+    def timed(job, a=args, blocks=0):
         for _ in range(a.warmup):
             job()
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
-        for k in range(a.steps):
-            ev[k][0].record(stream)
+        start.record(stream)
+        for _ in range(a.steps):
             job()
-            ev[k][1].record(stream)
+        end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        per = sorted(x.elapsed_time(y) for x, y in ev)
-        spread[id(job)] = {"step_ms_median": round(per[len(per) // 2], 5), "step_ms_min": round(per[0], 5),
-                           "step_ms_max": round(per[-1], 5)}
-        return sum(per) / a.steps, wall
+        per_step = start.elapsed_time(end) / a.steps
+        if blocks:
+            nb = min(20, a.steps)
+            runs = []
+            for _ in range(blocks):
+                s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s0.record(stream)
+                for _ in range(nb):
+                    job()
+                s1.record(stream)
+                torch.cuda.synchronize()
+                runs.append(s0.elapsed_time(s1) / nb)
+            runs.sort()
+            spread[id(job)] = {"blocks": blocks, "steps_per_block": nb, "step_ms_median": round(runs[len(runs) // 2], 5),
+                               "step_ms_min": round(runs[0], 5), "step_ms_max": round(runs[-1], 5)}
+        return per_step, wall
 
-    copy_ms, wall_copy = timed(copy_job) if args.only != "fused" else (0.0, 0.0)
-    fused_ms, wall_fused = timed(fused_job) if (fused_ok and args.only != "copy") else (0.0, 0.0)
+    copy_ms, wall_copy = timed(copy_job, blocks=3) if args.only != "fused" else (0.0, 0.0)
+    fused_ms, wall_fused = timed(fused_job, blocks=3) if (fused_ok and args.only != "copy") else (0.0, 0.0)
     step_ms = copy_ms + fused_ms
     wall = wall_copy + wall_fused
     if args.calib_copy_mib > 0:
