@@ -118,7 +118,8 @@ def _context(args, stream, timed, views, ins, geom):
 
     * the all-gather workload at the three program counts it is defined for;
     * destination groups 1/2/4 and the partitioned schedule (all-gather variants);
-    * the all-to-all on the same heap: W=8, 8 chunks of 1024x4096 fp16 per rank;
+    * the all-to-all on the same heap: W=8, 8 chunks of 1024x4096 fp16 per rank, tile and partitioned
+      schedules;
     * the all-gather at 16384x8192 per rank in fp16, bf16 and fp32 (2.4 / 2.4 / 4.8 GB per call);
     * the edge shapes: 1000x4100 fp16 (8-byte vectors, partial last column tile) at W=8, and the
       strided group of ranks 1, 3, 5, 7 (W=4) at 1000x4100 and 16384x8192.
@@ -180,6 +181,11 @@ def _context(args, stream, timed, views, ins, geom):
                      "traffic": _traffic(f"ag_a2a_kernel_w{AG_W}_{mc}x{AG_N}_f16_pmc.md", "ag_copy.hip", a2a_bytes),
                      "alg_bytes_per_launch": a2a_bytes, "avg_launch_us": round(launch_s * 1e6, 3)},
     }
+    # the partitioned schedule of the same exchange (program p copies one chunk to destination p mod W)
+    ms, _ = timed_sub(sub, timed, lambda: [ag.all_to_all_ex(views[j], AG_W, 0, 1, a2a_in[j], 0, mc, AG_N, AG_DTYPE,
+                                                            16, 512, 256, schedule="partitioned", stream=stream)
+                                           for j in range(AG_W)])
+    ctx["all_to_all"]["partitioned_16x512_256_programs_GBs"] = round(AG_W * a2a_bytes / (ms / 1e3) / 1e9, 1)
     del a2a_in
 
     sub3 = argparse.Namespace(**vars(sub))

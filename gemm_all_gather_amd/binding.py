@@ -97,6 +97,10 @@ _SIGNATURES = {
                       _c_int, _vp],
     "ag_plan_all_to_all": [ctypes.POINTER(Geometry), _c_int, _c_int, _c_int, _c_u64, _c_size, _c_i64, _c_i64,
                            _c_int, _c_int, _c_int, _c_int, ctypes.POINTER(Plan)],
+    "ag_all_to_all_ex": [_vp, _c_int, _c_int, _c_int, _vp, _c_size, _c_i64, _c_i64, _c_int, _c_int, _c_int,
+                         _c_int, ctypes.POINTER(CopyOptions), _vp],
+    "ag_plan_all_to_all_ex": [ctypes.POINTER(Geometry), _c_int, _c_int, _c_int, _c_u64, _c_size, _c_i64, _c_i64,
+                              _c_int, _c_int, _c_int, _c_int, ctypes.POINTER(CopyOptions), ctypes.POINTER(Plan)],
     "ag_gemm_all_gather": [_vp, _c_int, _c_int, _c_int, _vp, _c_i64, _vp, _c_i64, _c_size, _c_i64, _c_i64,
                            _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int, _vp],
     "ag_plan_gemm_all_gather": [ctypes.POINTER(Geometry), _c_int, _c_int, _c_int, _c_u64, _c_i64, _c_u64, _c_i64,
@@ -276,6 +280,24 @@ def all_to_all(heap: Heap, W, rank_start, rank_stride, input, out_offset, M_chun
                tile_m=0, tile_n=0, n_programs=0, stream=None) -> None:
     _check(lib().ag_all_to_all(heap.handle, W, rank_start, rank_stride, _ptr(input), out_offset, M_chunk, N,
                                _dtype(dtype), tile_m, tile_n, n_programs, _stream(stream)), "ag_all_to_all")
+
+
+def plan_all_to_all_ex(geom: Geometry, W, rank_start, rank_stride, input_addr, out_offset, M_chunk, N, dtype,
+                       tile_m=0, tile_n=0, n_programs=0, dest_group=0, schedule=0) -> Plan:
+    p = Plan()
+    o = _options(dest_group, schedule)
+    _check(lib().ag_plan_all_to_all_ex(ctypes.byref(geom), W, rank_start, rank_stride, _ptr(input_addr), out_offset,
+                                       M_chunk, N, _dtype(dtype), tile_m, tile_n, n_programs, ctypes.byref(o),
+                                       ctypes.byref(p)), "ag_plan_all_to_all_ex")
+    return p
+
+
+def all_to_all_ex(heap: Heap, W, rank_start, rank_stride, input, out_offset, M_chunk, N, dtype,
+                  tile_m=0, tile_n=0, n_programs=0, dest_group=0, schedule=0, stream=None) -> None:
+    o = _options(dest_group, schedule)
+    _check(lib().ag_all_to_all_ex(heap.handle, W, rank_start, rank_stride, _ptr(input), out_offset, M_chunk, N,
+                                  _dtype(dtype), tile_m, tile_n, n_programs, ctypes.byref(o), _stream(stream)),
+           "ag_all_to_all_ex")
 
 
 def plan_gemm_all_gather(geom: Geometry, W, rank_start, rank_stride, a_addr, lda, b_addr, ldb, out_offset,

@@ -109,7 +109,9 @@ struct TileRef {
 };
 
 // W destinations per tile; G destinations per wait (0: none).  PART: the
-// partitioned schedule (W = 1, the group size is a.world at run time).
+// partitioned schedule (W = 1, the group size is a.world at run time).  A
+// partitioned program of the all-to-all (a.chunk_bytes > 0) reads the chunk
+// its destination receives: chunk (g + i) mod W for destination i.
 template <int VEC, int W, int VPT, int G, bool PART>
 __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
 {
@@ -118,7 +120,12 @@ __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
     static_assert(G == 0 || G < W, "a group smaller than the destination count");
     static_assert(!PART || (W == 1 && G == 0), "a partitioned program has one destination");
 
-    const uint64_t input = reinterpret_cast<uint64_t>(a.input);
+    uint64_t input = reinterpret_cast<uint64_t>(a.input);
+    if constexpr (PART) {
+        int c = a.group_rank + static_cast<int>(blockIdx.x % a.world);   // < 2 * world
+        if (c >= static_cast<int>(a.world)) c -= static_cast<int>(a.world);
+        input += static_cast<uint64_t>(c) * a.chunk_bytes;
+    }
     const uint64_t block_bytes = static_cast<uint64_t>(a.rows) * a.row_bytes;
 
     // ---- tile-invariant lane geometry
@@ -466,7 +473,8 @@ CopyFn pick_a2a_world(int w, int vpt)
 
 CopyFn pick_kernel(int kind, int vec, int w, int g, int vpt, bool part)
 {
-    if (kind == kCopyAllToAll) {
+    // the partitioned all-to-all runs the partitioned copy kernel (one destination per program)
+    if (kind == kCopyAllToAll && !part) {
         if (g != 0) return nullptr;
         switch (vec) {
         case 16: return pick_a2a_world<16>(w, vpt);

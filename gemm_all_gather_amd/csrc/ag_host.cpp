@@ -357,7 +357,7 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
                     W, static_cast<unsigned long long>(blk), out_offset,
                     static_cast<unsigned long long>(geom->bytes_per_rank));
 
-    const bool part = !a2a && opt.schedule == AG_SCHEDULE_PARTITIONED;
+    const bool part = opt.schedule == AG_SCHEDULE_PARTITIONED;
     const uint64_t in_bytes = a2a ? W * blk : blk;
     ag_plan_t p{};
     p.group_rank = g;
@@ -395,7 +395,8 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     while (vec > e && ((row_bytes % vec) != 0 || (input_addr % vec) != 0 || (out_addr % vec) != 0)) vec /= 2;
     const uint64_t tile_row_bytes = static_cast<uint64_t>(tile_n) * e;
     const uint64_t tile_vecs = static_cast<uint64_t>(tile_m) * tile_row_bytes / vec;
-    const int max_vpt = a2a ? std::min(32 / vec, kCopyMaxVpt) : kCopyMaxVpt;   // all-to-all: <= 32 bytes per thread
+    // the all-to-all's tile schedule holds W tiles per thread: <= 32 bytes of each
+    const int max_vpt = (a2a && !part) ? std::min(32 / vec, kCopyMaxVpt) : kCopyMaxVpt;
     if (tile_vecs % 256 != 0 || tile_vecs / 256 > static_cast<uint64_t>(max_vpt))
         return fail(AG_ERR_UNSUPPORTED, "tile %dx%d holds %llu %d-byte vectors; 256 to %d are supported",
                     tile_m, tile_n, static_cast<unsigned long long>(tile_vecs), vec, 256 * max_vpt);
@@ -457,7 +458,7 @@ ag_status_t launch_copy_call(const ag_heap_t* heap, int kind, int W, int rank_st
     l.args.input = static_cast<const uint8_t*>(input);
     l.args.rank_block_offset = p.rank_block_offset;
     l.args.row_bytes = static_cast<uint64_t>(N) * e;
-    l.args.chunk_bytes = static_cast<uint64_t>(M) * N * e;
+    l.args.chunk_bytes = kind == ag::kCopyAllToAll ? static_cast<uint64_t>(M) * N * e : 0;
     l.args.rows = static_cast<uint32_t>(M);
     l.args.tile_m = static_cast<uint32_t>(p.tile_m);
     l.args.tile_row_bytes = static_cast<uint32_t>(p.tile_n) * e;
@@ -511,6 +512,15 @@ ag_status_t ag_plan_all_to_all(const ag_heap_geometry_t* geom, int W, int rank_s
                      tile_m, tile_n, n_programs, nullptr, plan);
 }
 
+ag_status_t ag_plan_all_to_all_ex(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
+                                  uint64_t input_addr, size_t out_offset, int64_t M_chunk, int64_t N,
+                                  ag_dtype_t dtype, int tile_m, int tile_n, int n_programs,
+                                  const ag_copy_options_t* options, ag_plan_t* plan)
+{
+    return plan_copy(geom, ag::kCopyAllToAll, W, rank_start, rank_stride, input_addr, out_offset, M_chunk, N, dtype,
+                     tile_m, tile_n, n_programs, options, plan);
+}
+
 ag_status_t ag_all_gather(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
                           const void* input, size_t out_offset, int64_t M_local, int64_t N,
                           ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, void* stream)
@@ -534,6 +544,15 @@ ag_status_t ag_all_to_all(const ag_heap_t* heap, int W, int rank_start, int rank
 {
     return launch_copy_call(heap, ag::kCopyAllToAll, W, rank_start, rank_stride, input, out_offset, M_chunk, N,
                             dtype, tile_m, tile_n, n_programs, nullptr, stream);
+}
+
+ag_status_t ag_all_to_all_ex(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                             const void* input, size_t out_offset, int64_t M_chunk, int64_t N,
+                             ag_dtype_t dtype, int tile_m, int tile_n, int n_programs,
+                             const ag_copy_options_t* options, void* stream)
+{
+    return launch_copy_call(heap, ag::kCopyAllToAll, W, rank_start, rank_stride, input, out_offset, M_chunk, N,
+                            dtype, tile_m, tile_n, n_programs, options, stream);
 }
 
 // ---------------------------------------------------------------------------

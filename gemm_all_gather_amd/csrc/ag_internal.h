@@ -13,7 +13,7 @@ struct CopyKernelArgs {
     const uint8_t* input;         // rank's M x N block (all-to-all: W such chunks), row-major
     uint64_t rank_block_offset;   // out_offset + g*M*N*e, same in every region
     uint64_t row_bytes;           // N*e
-    uint64_t chunk_bytes;         // all-to-all: M*N*e between consecutive input chunks
+    uint64_t chunk_bytes;         // all-to-all: M*N*e between consecutive input chunks (all-gather: 0)
     uint32_t rows;                // M (M_local, or M_chunk for the all-to-all)
     uint32_t tile_m;              // rows per tile
     uint32_t tile_row_bytes;      // tile_n*e

@@ -262,6 +262,24 @@ ag_status_t ag_plan_all_to_all(const ag_heap_geometry_t* geom, int W, int rank_s
                                uint64_t input_addr, size_t out_offset, int64_t M_chunk, int64_t N,
                                ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, ag_plan_t* plan);
 
+/* ag_all_to_all with options (NULL or all-zero = ag_all_to_all).  Same
+ * result.  dest_group must be 0 (AG_ERR_INVALID_ARG otherwise).  schedule
+ * AG_SCHEDULE_PARTITIONED (the partitioned schedule of ag_all_gather_ex
+ * applied to the exchange): program p owns destination i = p mod W of the
+ * rotated order and copies chunk (g + i) mod W there, the programs of one
+ * destination walking all tiles among themselves; every chunk is read once.
+ * n_programs is rounded down to a multiple of W (at least W); tiles may
+ * then hold up to 8 vectors per thread, as for ag_all_gather. */
+ag_status_t ag_all_to_all_ex(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                             const void* input, size_t out_offset, int64_t M_chunk, int64_t N,
+                             ag_dtype_t dtype, int tile_m, int tile_n, int n_programs,
+                             const ag_copy_options_t* options, void* stream);
+
+ag_status_t ag_plan_all_to_all_ex(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
+                                  uint64_t input_addr, size_t out_offset, int64_t M_chunk, int64_t N,
+                                  ag_dtype_t dtype, int tile_m, int tile_n, int n_programs,
+                                  const ag_copy_options_t* options, ag_plan_t* plan);
+
 /* ------------------------------------------------------------------------
  * Fused GEMM + all-gather (ROCm/iris #626 "Assembly" table and "Benchmark").
  *

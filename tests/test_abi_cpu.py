@@ -325,3 +325,39 @@ def test_plan_all_to_all_input_may_not_overlap_any_output():
     assert status_of(plan_a2a, g=g, inp=own)[0] == ag.AG_ERR_INVALID_ARG
     assert status_of(plan_a2a, g=g, inp=SLAB + 6 * g.bytes_per_rank + 8 * blk)[0] == ag.AG_OK   # past the block
     assert status_of(plan_a2a, g=g, inp=SLAB + 6 * g.bytes_per_rank + 8 * blk - 2)[0] == ag.AG_ERR_INVALID_ARG
+
+
+def plan_a2a_ex(g=None, W=8, start=0, stride=1, inp=INPUT, off=0, M=128, N=4096, dtype="f16", tm=0, tn=0, progs=0,
+                group=0, sched=0):
+    return ag.plan_all_to_all_ex(g or geom(), W, start, stride, inp, off, M, N, dtype, tm, tn, progs,
+                                 dest_group=group, schedule=sched)
+
+
+def test_plan_all_to_all_ex_defaults_equal_the_plain_call():
+    a, b = plan_a2a(g=geom(rank=3)), plan_a2a_ex(g=geom(rank=3))
+    assert a.as_dict() == b.as_dict()
+
+
+@pytest.mark.parametrize("W,progs,grid", [(8, 256, 256), (8, 100, 96), (8, 5, 8), (3, 256, 255), (1, 7, 7)])
+def test_plan_all_to_all_partitioned_programs(W, progs, grid):
+    p = plan_a2a_ex(W=W, progs=progs, sched="partitioned")
+    assert p.schedule == ag.AG_SCHEDULE_PARTITIONED
+    assert p.n_programs == grid and p.n_programs % W == 0 and p.threads == 256
+    blk = 128 * 4096 * 2
+    assert p.bytes_read == W * blk and p.bytes_written == W * blk    # every chunk read once
+
+
+def test_plan_all_to_all_partitioned_allows_more_vectors_per_thread():
+    # one tile in registers per program: 4 vectors of 16 bytes, beyond the tile schedule's 32 bytes of each chunk
+    assert status_of(plan_a2a_ex, tm=32, tn=256)[0] == ag.AG_ERR_UNSUPPORTED
+    p = plan_a2a_ex(tm=32, tn=256, sched="partitioned")
+    assert (p.vec_bytes, p.vectors_per_thread) == (16, 4)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(group=2), ag.AG_ERR_INVALID_ARG),                          # the all-to-all takes no destination groups
+    (dict(group=2, sched="partitioned"), ag.AG_ERR_INVALID_ARG),
+    (dict(sched=7), ag.AG_ERR_INVALID_ARG),
+])
+def test_plan_all_to_all_ex_rejects(kw, status):
+    assert status_of(plan_a2a_ex, **kw)[0] == status

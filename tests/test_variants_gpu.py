@@ -55,10 +55,10 @@ def _gather_ex(R, S, W, start, stride, M, N, dtype, off, tile=(0, 0), programs=0
         th.close()
 
 
-def _a2a(R, S, W, start, stride, M, N, dtype, off, tile=(0, 0), programs=0, seed=0, streams=False):
+def _a2a(R, S, W, start, stride, M, N, dtype, off, tile=(0, 0), programs=0, seed=0, streams=False, sched=0):
     require_gpu()
     log(f"all_to_all R={R} S={S} W={W} group=({start},{stride}) M_chunk={M} N={N} {dtype} off={off} tile={tile} "
-        f"programs={programs} seed={seed}")
+        f"programs={programs} seed={seed} schedule={sched}")
     th = TorchHeap(R, S)
     try:
         before = th.fill_random(seed + 9)
@@ -66,8 +66,8 @@ def _a2a(R, S, W, start, stride, M, N, dtype, off, tile=(0, 0), programs=0, seed
         dev = [to_device(x) for x in ins]
         ss = [torch.cuda.Stream() for _ in range(W)] if streams else [None] * W
         for g in range(W):
-            ag.all_to_all(th.view(start + g * stride), W, start, stride, dev[g], off, M, N, dtype, tile[0], tile[1],
-                          programs, ss[g])
+            ag.all_to_all_ex(th.view(start + g * stride), W, start, stride, dev[g], off, M, N, dtype, tile[0],
+                             tile[1], programs, schedule=sched, stream=ss[g])
         torch.cuda.synchronize()
         _compare(th.host(), all_to_all_oracle(before, S, ins, start, stride, off), S)
     finally:
@@ -188,3 +188,19 @@ def test_all_to_all_validation():
         assert exc.value.status == ag.AG_ERR_INVALID_ARG
     finally:
         th.close()
+
+
+@pytest.mark.parametrize("W,start,stride", [(1, 0, 1), (2, 0, 1), (3, 1, 2), (5, 2, 1), (8, 0, 1)])
+@pytest.mark.parametrize("M,N,dtype,tile,programs", [(7, 300, "f16", (8, 256), 1), (64, 256, "bf16", (32, 256), 16),
+                                                      (33, 1000, "f32", (8, 256), 24), (9, 264, "f16", (4, 512), 10_000)])
+def test_all_to_all_partitioned(W, start, stride, M, N, dtype, tile, programs):
+    e = E[dtype]
+    off = 64
+    _a2a(8, _size(W, M, N, e, off), W, start, stride, M, N, dtype, off, tile, programs, seed=W * 10 + M,
+         sched="partitioned")
+
+
+def test_all_to_all_partitioned_streams_and_full_size():
+    _a2a(8, _size(4, 125, 4100, 2, 64), 4, 1, 2, 125, 4100, "f16", 64, (8, 256), 64, seed=13, streams=True,
+         sched="partitioned")
+    _a2a(8, _size(8, 1024, 4096, 2, 0), 8, 0, 1, 1024, 4096, "f16", 0, (8, 512), 256, seed=14, sched="partitioned")
