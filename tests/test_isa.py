@@ -78,12 +78,15 @@ def _outermost(loops):
     return max(loops, key=lambda x: x[1] - x[0])
 
 
-COPY_CASES = [("16", "8", "1"), ("16", "8", "2"), ("8", "8", "2"), ("16", "4", "1"), ("4", "2", "4")]
+# (vector bytes, W, vectors per thread, partitioned); the partitioned kernel (one destination per program,
+# also the all-to-all's partitioned schedule) has W = 1
+COPY_CASES = [("16", "8", "1", "0"), ("16", "8", "2", "0"), ("8", "8", "2", "0"), ("16", "4", "1", "0"),
+              ("4", "2", "4", "0"), ("16", "1", "1", "1"), ("16", "1", "2", "1")]
 
 
-@pytest.mark.parametrize("vec,w,vpt", COPY_CASES)
-def test_copy_kernel_hoists_bases_and_never_drains_before_a_store(asm, vec, w, vpt):
-    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_copy_kernelILi{vec}ELi{w}ELi{vpt}ELi0ELb0E")
+@pytest.mark.parametrize("vec,w,vpt,part", COPY_CASES)
+def test_copy_kernel_hoists_bases_and_never_drains_before_a_store(asm, vec, w, vpt, part):
+    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_copy_kernelILi{vec}ELi{w}ELi{vpt}ELi0ELb{part}E")
     W, VPT = int(w), int(vpt)
     loops = _loops(lines)
     assert loops, "tile loop not found"
