@@ -26,7 +26,7 @@ What it computes (sources are the three pages on the iris all-gather):
   rank's C_j = A_j . B_j, rounded once to the 16-bit output type, then
   gathered exactly as above.  The dot products are formed in float64 (the
   "exact" value up to negligible rounding); the kernel under test accumulates
-  in float32 and is judged against this within a tolerance.
+  in float32 and is compared with this within a tolerance.
 
 Readings of points the pages leave open (each is repeated in the project's
 design notes):

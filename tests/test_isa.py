@@ -1,6 +1,6 @@
 """Code-generation checks on our own gfx950 assembly (compile only, no GPU).
 
-The pages judge the hoisting by the generated code (ROCm/iris #626,
+The pages assess the hoisting by the generated code (ROCm/iris #626,
 "Assembly" table; ROCm/iris #594, "Compiler inspection and grouping"):
 heap-base loads precede the tile loop, the only load inside it is the input
 tile, no destination store is preceded by a full drain, the destination
