@@ -94,13 +94,13 @@ typedef struct ag_plan {
     int32_t schedule;            /* copy kernels: ag_schedule_t of the launch */
 } ag_plan_t;
 
-/* Tile schedules of the all-gather. */
+/* Tile schedules of the all-gather (ag_all_gather_ex) and the all-to-all (ag_all_to_all_ex). */
 typedef enum ag_schedule {
     AG_SCHEDULE_TILES = 0,       /* each program walks tiles and stores every tile to all W destinations */
     AG_SCHEDULE_PARTITIONED = 1  /* each program owns one destination and walks the tiles for it alone */
 } ag_schedule_t;
 
-/* Options of ag_all_gather_ex; all-zero (or a NULL pointer) is ag_all_gather. */
+/* Options of ag_all_gather_ex and ag_all_to_all_ex; all-zero (or a NULL pointer) is the plain call. */
 typedef struct ag_copy_options {
     int32_t dest_group;   /* 0: one straight run of W destination stores per tile (default).
                              1, 2 or 4 (< W): store that many destinations, then wait until the
