@@ -56,11 +56,17 @@ class Plan(ctypes.Structure):
 
 AG_SCHEDULE_TILES, AG_SCHEDULE_PARTITIONED = 0, 1
 SCHEDULES = {"tiles": AG_SCHEDULE_TILES, "partitioned": AG_SCHEDULE_PARTITIONED}
+AG_B_K_CONTIGUOUS, AG_B_N_CONTIGUOUS = 0, 1
+B_LAYOUTS = {"k": AG_B_K_CONTIGUOUS, "n": AG_B_N_CONTIGUOUS}
 
 
 class CopyOptions(ctypes.Structure):
     _fields_ = [("dest_group", ctypes.c_int32), ("schedule", ctypes.c_int32),
                 ("reserved", ctypes.c_int32 * 6)]
+
+
+class GemmOptions(ctypes.Structure):
+    _fields_ = [("b_layout", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
 
 
 def _options(dest_group=0, schedule=0) -> CopyOptions:
@@ -106,6 +112,11 @@ _SIGNATURES = {
     "ag_plan_gemm_all_gather": [ctypes.POINTER(Geometry), _c_int, _c_int, _c_int, _c_u64, _c_i64, _c_u64, _c_i64,
                                 _c_size, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int,
                                 ctypes.POINTER(Plan)],
+    "ag_gemm_all_gather_ex": [_vp, _c_int, _c_int, _c_int, _vp, _c_i64, _vp, _c_i64, _c_size, _c_i64, _c_i64,
+                              _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int, ctypes.POINTER(GemmOptions), _vp],
+    "ag_plan_gemm_all_gather_ex": [ctypes.POINTER(Geometry), _c_int, _c_int, _c_int, _c_u64, _c_i64, _c_u64,
+                                   _c_i64, _c_size, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                   ctypes.POINTER(GemmOptions), ctypes.POINTER(Plan)],
 }
 
 
@@ -314,3 +325,29 @@ def gemm_all_gather(heap: Heap, W, rank_start, rank_stride, A, lda, B, ldb, out_
     _check(lib().ag_gemm_all_gather(heap.handle, W, rank_start, rank_stride, _ptr(A), lda, _ptr(B), ldb,
                                     out_offset, M_local, N, K, _dtype(dtype), tile_m, tile_n, tile_k, n_programs,
                                     _stream(stream)), "ag_gemm_all_gather")
+
+
+def _gemm_options(b_layout=0) -> GemmOptions:
+    o = GemmOptions()
+    o.b_layout = B_LAYOUTS[b_layout] if isinstance(b_layout, str) else b_layout
+    return o
+
+
+def plan_gemm_all_gather_ex(geom: Geometry, W, rank_start, rank_stride, a_addr, lda, b_addr, ldb, out_offset,
+                            M_local, N, K, dtype, tile_m=0, tile_n=0, tile_k=0, n_programs=0, b_layout=0) -> Plan:
+    """b_layout: "k" (element (k,n) at B[n*ldb + k]) or "n" (at B[k*ldb + n])."""
+    p = Plan()
+    o = _gemm_options(b_layout)
+    _check(lib().ag_plan_gemm_all_gather_ex(ctypes.byref(geom), W, rank_start, rank_stride, _ptr(a_addr), lda,
+                                            _ptr(b_addr), ldb, out_offset, M_local, N, K, _dtype(dtype), tile_m,
+                                            tile_n, tile_k, n_programs, ctypes.byref(o), ctypes.byref(p)),
+           "ag_plan_gemm_all_gather_ex")
+    return p
+
+
+def gemm_all_gather_ex(heap: Heap, W, rank_start, rank_stride, A, lda, B, ldb, out_offset, M_local, N, K, dtype,
+                       tile_m=0, tile_n=0, tile_k=0, n_programs=0, b_layout=0, stream=None) -> None:
+    o = _gemm_options(b_layout)
+    _check(lib().ag_gemm_all_gather_ex(heap.handle, W, rank_start, rank_stride, _ptr(A), lda, _ptr(B), ldb,
+                                       out_offset, M_local, N, K, _dtype(dtype), tile_m, tile_n, tile_k, n_programs,
+                                       ctypes.byref(o), _stream(stream)), "ag_gemm_all_gather_ex")

@@ -191,6 +191,34 @@ struct Frag {
     }
 };
 
+// B fragment of a 16-column block from an N-contiguous stage (rows of k,
+// TN columns each): two transposing reads, k 0..3 then k 4..7 of the lane's
+// 8-row group.  ds_read_b64_tr_b16 gives lane i of each 16-lane group the
+// (i & 3)-th 16-bit element of the 8-byte chunk addressed by lane
+// 4*j + (i >> 2), for j = 0..3: with lane p addressing row (p >> 2) at
+// columns 4*(p & 3) .. +3, lane i receives column i of rows 0..3.  lo and hi
+// address the two halves; the block's column offset is the immediate.
+template <class C>
+struct FragT {
+    template <class V>
+    static __device__ __forceinline__ void read(V& dst, uint32_t lo, uint32_t hi, int block)
+    {
+        u32x2 a, b;
+        switch (block) {   // the offset must be an immediate
+#define AG_FRAGT_CASE(n)                                                                                  \
+    case n:                                                                                               \
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(a) : "v"(lo), "i"(n * 32));            \
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(b) : "v"(hi), "i"(n * 32));            \
+        break;
+            AG_FRAGT_CASE(0) AG_FRAGT_CASE(1) AG_FRAGT_CASE(2) AG_FRAGT_CASE(3)
+            AG_FRAGT_CASE(4) AG_FRAGT_CASE(5) AG_FRAGT_CASE(6) AG_FRAGT_CASE(7)
+#undef AG_FRAGT_CASE
+        default: a = u32x2{0u, 0u}; b = a; break;
+        }
+        dst = __builtin_bit_cast(V, u32x4{a.x, a.y, b.x, b.y});
+    }
+};
+
 // One K stage of the A and B tiles, global -> LDS.  Wave instruction i of the
 // stage moves RPI rows x ROW_BYTES (A rows for i < A_INSTR, then B rows) to
 // LDS bytes [i*1024, i*1024 + 1024) of the slot; wave w issues instructions
@@ -230,28 +258,65 @@ struct Stage {
             }
         }
     }
+    // N-contiguous B: the stage is BK rows of k with TN*2 bytes each, dense in
+    // LDS; byte x of the stage region comes from row x / (TN*2), byte column
+    // x % (TN*2) of the tile's columns.  lane16 = 16 * lane.
+    static __device__ __forceinline__ uint32_t bt_off(int i, uint32_t lane16, uint32_t ld2)
+    {
+        constexpr uint32_t RB = C::TN * 2;
+        const uint32_t x = static_cast<uint32_t>(i) * 1024u + lane16;
+        const uint32_t row = x / RB;
+        return row * ld2 + (x - row * RB);
+    }
+    // The descriptor of N-contiguous stage kt starts at its first row: the
+    // buffer range check covers the VGPR and immediate offsets but not the
+    // SGPR one, so the stage offset goes into the base, and the columns past N
+    // of the last row of B read as zero instead of past the end of B.
+    static __device__ __forceinline__ __amdgpu_buffer_rsrc_t bt_rsrc(uint64_t base, uint64_t records, int kt,
+                                                                     uint32_t ld2)
+    {
+        const uint64_t o = static_cast<uint64_t>(kt) * static_cast<uint64_t>(C::BK * ld2);
+        return make_rsrc(base + o, records > o ? records - o : 0);
+    }
+    static __device__ __forceinline__ void load_part_bt(uint64_t base, uint64_t records, uint8_t* slot, int kt,
+                                                        int wp, uint32_t lane16, uint32_t ld2)
+    {
+        constexpr int H = C::NW / 2;
+        const __amdgpu_buffer_rsrc_t r = bt_rsrc(base, records, kt, ld2);
+        asm volatile("" : "+v"(lane16), "+s"(ld2));
+#pragma unroll
+        for (int j = 0; j < C::B_INSTR / H; ++j) {
+            const int i = wp + H * j;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (AG_LDS void*)(slot + (C::A_INSTR + i) * 1024), 16,
+                                                     bt_off(i, lane16, ld2), 0, 0, 0);
+        }
+    }
     static __device__ __forceinline__ void load(uint64_t a_base, uint64_t a_records, uint64_t b_base,
                                                 uint64_t b_records, uint8_t* slot, int kt, int wave,
-                                                const uint32_t* voff)
+                                                const uint32_t* voff, bool bt, uint32_t ldb2)
     {
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, a_records);
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, b_records);
         const uint32_t soff = static_cast<uint32_t>(kt) * C::ROW_BYTES;   // k0 * 2 bytes
+        // K-contiguous B steps along its rows like A; N-contiguous B by whole rows of k
+        const __amdgpu_buffer_rsrc_t rb = bt ? bt_rsrc(b_base, b_records, kt, ldb2) : make_rsrc(b_base, b_records);
+        const uint32_t bsoff = bt ? 0u : soff;
 #pragma unroll
         for (int j = 0; j < C::MAXL; ++j) {
             const int i = wave + C::NW * j;
             if (j < C::A_J) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (AG_LDS void*)(slot + i * 1024), 16, voff[j], soff, 0, 0);
             } else if (i < C::INSTR) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (AG_LDS void*)(slot + i * 1024), 16, voff[j], soff, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (AG_LDS void*)(slot + i * 1024), 16, voff[j], bsoff, 0, 0);
             }
         }
     }
 };
 
-template <bool BF16, int W, class C>
+// BT: B is N-contiguous (element (k,n) at B[k*ldb + n]); otherwise K-contiguous.
+template <bool BF16, int W, class C, bool BT>
 __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
 {
+    static_assert(!BT || C::ALT || C::BM + 2 * C::BN < 16, "two B reads per block must fit the 4-bit LDS counter");
     using M = Mfma<BF16>;
     using V = typename M::V;
     __shared__ __attribute__((aligned(1024))) uint8_t ring[C::NS][C::STAGE];
@@ -292,9 +357,16 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
 #pragma unroll
     for (int j = 0; j < C::MAXL; ++j) {
         const int i = wave + C::NW * j;
-        voff[j] = (j < C::A_J) ? (static_cast<uint32_t>(i * C::RPI) + lrow) * lda2 + lchunk * 16u
-                               : (static_cast<uint32_t>((i - C::A_INSTR) * C::RPI) + lrow) * ldb2 + lchunk * 16u;
+        if (BT && j >= C::A_J)
+            voff[j] = Stage<C>::bt_off(i - C::A_INSTR, static_cast<uint32_t>(lane) * 16u, ldb2);
+        else
+            voff[j] = (j < C::A_J) ? (static_cast<uint32_t>(i * C::RPI) + lrow) * lda2 + lchunk * 16u
+                                   : (static_cast<uint32_t>((i - C::A_INSTR) * C::RPI) + lrow) * ldb2 + lchunk * 16u;
     }
+    // N-contiguous B fragments: lane (q = lane >> 4, p = lane & 15) addresses row 8q + (p >> 2) of its
+    // K-step, columns 4*(p & 3) .. +3 of its wave's first block
+    const uint32_t bt_lane = static_cast<uint32_t>((8 * (lane >> 4) + ((lane & 15) >> 2)) * (C::TN * 2)) +
+                             static_cast<uint32_t>(wn * C::WTN + 4 * (lane & 3)) * 2u;
     // fragment of MFMA K-step kk: row (lane & 15) of a 16-row block, logical chunk kk*4 + (lane >> 4)
     uint32_t frag_off[C::KSUB];
 #pragma unroll
@@ -326,8 +398,10 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
 
         const uint64_t a_base = reinterpret_cast<uint64_t>(a.A) + static_cast<uint64_t>(m0) * lda2;
         const uint64_t a_records = static_cast<uint64_t>(a.M - m0) * lda2;
-        const uint64_t b_base = reinterpret_cast<uint64_t>(a.B) + static_cast<uint64_t>(n0) * ldb2;
-        const uint64_t b_records = static_cast<uint64_t>(a.N - n0) * ldb2;
+        const uint64_t b_base = BT ? reinterpret_cast<uint64_t>(a.B) + static_cast<uint64_t>(n0) * 2u
+                                   : reinterpret_cast<uint64_t>(a.B) + static_cast<uint64_t>(n0) * ldb2;
+        const uint64_t b_records = BT ? static_cast<uint64_t>(a.K - 1) * ldb2 + static_cast<uint64_t>(a.N - n0) * 2u
+                                      : static_cast<uint64_t>(a.N - n0) * ldb2;
 
         f32x4 acc[C::BM][C::BN];
 #pragma unroll
@@ -343,11 +417,15 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
             if constexpr (C::ALT) {
                 if (half == (kt & 1)) {   // whole stage (prologue)
                     Stage<C>::load_part(true, a_base, live ? a_records : 0, &ring[slot][0], kt, wp, la, lda2);
-                    Stage<C>::load_part(false, b_base, live ? b_records : 0, &ring[slot][0], kt, wp, lb, ldb2);
+                    if constexpr (BT)
+                        Stage<C>::load_part_bt(b_base, live ? b_records : 0, &ring[slot][0], kt, wp,
+                                               static_cast<uint32_t>(lane) * 16u, ldb2);
+                    else
+                        Stage<C>::load_part(false, b_base, live ? b_records : 0, &ring[slot][0], kt, wp, lb, ldb2);
                 }
             } else {
                 Stage<C>::load(a_base, live ? a_records : 0, b_base, live ? b_records : 0, &ring[slot][0], kt, wave,
-                               voff);
+                               voff, BT, ldb2);
             }
         };
         // Fragment reads are inline assembly: the compiler cannot tell these
@@ -360,8 +438,15 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
             const uint32_t sb = sbase + b_row0 + frag_off[kk];
 #pragma unroll
             for (int bm = 0; bm < C::BM; ++bm) Frag<C>::read(fa[f][bm], sa, bm);
+            if constexpr (BT) {
+                const uint32_t lo = sbase + C::A_BYTES + bt_lane + static_cast<uint32_t>(kk * 32 * C::TN * 2);
+                const uint32_t hi = lo + static_cast<uint32_t>(4 * C::TN * 2);
 #pragma unroll
-            for (int bn = 0; bn < C::BN; ++bn) Frag<C>::read(fb[f][bn], sb, bn);
+                for (int bn = 0; bn < C::BN; ++bn) FragT<C>::read(fb[f][bn], lo, hi, bn);
+            } else {
+#pragma unroll
+                for (int bn = 0; bn < C::BN; ++bn) Frag<C>::read(fb[f][bn], sb, bn);
+            }
         };
         auto mfmas = [&](int f) {
 #pragma unroll
@@ -395,8 +480,12 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
             for (int kk = 0; kk < C::KSUB; ++kk) {
                 if (kk == 0 && s >= 1 && half != ((s - 1) & 1)) {
                     const int kn = s + 1;
-                    Stage<C>::load_part(false, b_base, kn < kt_total ? b_records : 0, &ring[next_slot][0], kn, wp,
-                                        lb, ldb2);
+                    if constexpr (BT)
+                        Stage<C>::load_part_bt(b_base, kn < kt_total ? b_records : 0, &ring[next_slot][0], kn, wp,
+                                               static_cast<uint32_t>(lane) * 16u, ldb2);
+                    else
+                        Stage<C>::load_part(false, b_base, kn < kt_total ? b_records : 0, &ring[next_slot][0], kn,
+                                            wp, lb, ldb2);
                 }
                 read_frags(slot, kk, 0);
                 __builtin_amdgcn_sched_barrier(0);
@@ -428,7 +517,8 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
                     // possibly at the stage boundary) have landed; the reads
                     // just issued may still be in flight
                     __builtin_amdgcn_sched_barrier(0);
-                    wait_lgkmcnt<C::BM + C::BN>();
+                    // (alternating-loader tiles run stage_alt, never this path)
+                    wait_lgkmcnt<C::ALT ? 0 : C::BM + (BT ? 2 : 1) * C::BN>();
                     __builtin_amdgcn_sched_barrier(0);
                 } else {
                     __builtin_amdgcn_sched_barrier(0);
@@ -552,29 +642,31 @@ using CfgT128x128 = Cfg<AG_GEMM_CFG_128x128>;
 
 using GemmFn = void (*)(GemmKernelArgs);
 
-template <bool BF16, class C>
+template <bool BF16, class C, bool BT>
 GemmFn pick_world(int w)
 {
     switch (w) {
-    case 1: return ag_gemm_kernel<BF16, 1, C>;
-    case 2: return ag_gemm_kernel<BF16, 2, C>;
-    case 3: return ag_gemm_kernel<BF16, 3, C>;
-    case 4: return ag_gemm_kernel<BF16, 4, C>;
-    case 5: return ag_gemm_kernel<BF16, 5, C>;
-    case 6: return ag_gemm_kernel<BF16, 6, C>;
-    case 7: return ag_gemm_kernel<BF16, 7, C>;
-    case 8: return ag_gemm_kernel<BF16, 8, C>;
+    case 1: return ag_gemm_kernel<BF16, 1, C, BT>;
+    case 2: return ag_gemm_kernel<BF16, 2, C, BT>;
+    case 3: return ag_gemm_kernel<BF16, 3, C, BT>;
+    case 4: return ag_gemm_kernel<BF16, 4, C, BT>;
+    case 5: return ag_gemm_kernel<BF16, 5, C, BT>;
+    case 6: return ag_gemm_kernel<BF16, 6, C, BT>;
+    case 7: return ag_gemm_kernel<BF16, 7, C, BT>;
+    case 8: return ag_gemm_kernel<BF16, 8, C, BT>;
     default: return nullptr;
     }
 }
 
+// N-contiguous B has kernels for the 256x224 and 128x128 tiles (256x256 would
+// need more LDS reads per K-step than the 4-bit LDS counter tracks)
 template <bool BF16>
-GemmFn pick_cfg(int cfg, int w)
+GemmFn pick_cfg(int cfg, int w, bool bt)
 {
     switch (cfg) {
-    case kGemmTile256x256: return pick_world<BF16, CfgT256x256>(w);
-    case kGemmTile256x224: return pick_world<BF16, CfgT256x224>(w);
-    case kGemmTile128x128: return pick_world<BF16, CfgT128x128>(w);
+    case kGemmTile256x256: return bt ? nullptr : pick_world<BF16, CfgT256x256, false>(w);
+    case kGemmTile256x224: return bt ? pick_world<BF16, CfgT256x224, true>(w) : pick_world<BF16, CfgT256x224, false>(w);
+    case kGemmTile128x128: return bt ? pick_world<BF16, CfgT128x128, true>(w) : pick_world<BF16, CfgT128x128, false>(w);
     default: return nullptr;
     }
 }
@@ -592,7 +684,8 @@ void gemm_resources(int cfg, int* threads, int* lds_bytes)
 
 hipError_t launch_gemm(const GemmLaunch& l, hipStream_t stream)
 {
-    GemmFn fn = l.bf16 ? pick_cfg<true>(l.cfg, l.world) : pick_cfg<false>(l.cfg, l.world);
+    GemmFn fn = l.bf16 ? pick_cfg<true>(l.cfg, l.world, l.b_n_contiguous != 0)
+                       : pick_cfg<false>(l.cfg, l.world, l.b_n_contiguous != 0);
     if (fn == nullptr || l.grid < 1) return hipErrorInvalidValue;
     int threads = 0, lds = 0;
     gemm_resources(l.cfg, &threads, &lds);

@@ -559,11 +559,15 @@ ag_status_t ag_all_to_all_ex(const ag_heap_t* heap, int W, int rank_start, int r
 // fused GEMM + all-gather
 // ---------------------------------------------------------------------------
 
-ag_status_t ag_plan_gemm_all_gather(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
-                                    uint64_t a_addr, int64_t lda, uint64_t b_addr, int64_t ldb,
-                                    size_t out_offset, int64_t M_local, int64_t N, int64_t K,
-                                    ag_dtype_t dtype, int tile_m, int tile_n, int tile_k,
-                                    int n_programs, ag_plan_t* plan)
+}  // extern "C"
+
+namespace {
+
+// bt: B stored N-contiguous (element (k,n) at B[k*ldb + n]); otherwise K-contiguous.
+ag_status_t plan_gemm(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride, uint64_t a_addr,
+                      int64_t lda, uint64_t b_addr, int64_t ldb, size_t out_offset, int64_t M_local, int64_t N,
+                      int64_t K, ag_dtype_t dtype, int tile_m, int tile_n, int tile_k, int n_programs, bool bt,
+                      ag_plan_t* plan)
 {
     ag_status_t s = check_geometry(geom);
     if (s != AG_OK) return s;
@@ -581,8 +585,12 @@ ag_status_t ag_plan_gemm_all_gather(const ag_heap_geometry_t* geom, int W, int r
         return fail(AG_ERR_UNSUPPORTED, "M_local, N or K > 2^30");
     if (K % 64 != 0) return fail(AG_ERR_UNSUPPORTED, "K %lld is not a multiple of 64", static_cast<long long>(K));
     if (N % 8 != 0) return fail(AG_ERR_UNSUPPORTED, "N %lld is not a multiple of 8", static_cast<long long>(N));
-    if (lda < K || ldb < K) return fail(AG_ERR_INVALID_ARG, "lda %lld or ldb %lld < K %lld",
-                                        static_cast<long long>(lda), static_cast<long long>(ldb), static_cast<long long>(K));
+    if (lda < K) return fail(AG_ERR_INVALID_ARG, "lda %lld < K %lld", static_cast<long long>(lda),
+                             static_cast<long long>(K));
+    if (!bt && ldb < K) return fail(AG_ERR_INVALID_ARG, "ldb %lld < K %lld (B K-contiguous)",
+                                    static_cast<long long>(ldb), static_cast<long long>(K));
+    if (bt && ldb < N) return fail(AG_ERR_INVALID_ARG, "ldb %lld < N %lld (B N-contiguous)",
+                                   static_cast<long long>(ldb), static_cast<long long>(N));
     if (lda % 8 != 0 || ldb % 8 != 0) return fail(AG_ERR_UNSUPPORTED, "lda and ldb must be multiples of 8");
     if (out_offset % 16 != 0) return fail(AG_ERR_UNSUPPORTED, "out_offset %zu is not a multiple of 16", out_offset);
     const uint64_t row_bytes = static_cast<uint64_t>(N) * 2;
@@ -595,6 +603,8 @@ ag_status_t ag_plan_gemm_all_gather(const ag_heap_geometry_t* geom, int W, int r
     struct TileCfg { int tm, tn, id; };
     static const TileCfg kTiles[] = {{256, 256, ag::kGemmTile256x256}, {256, 224, ag::kGemmTile256x224},
                                      {128, 128, ag::kGemmTile128x128}};
+    // an N-contiguous B reads two LDS fragments per 16 columns: no 256x256 kernel for it
+    auto available = [&](const TileCfg& t) { return !(bt && t.id == ag::kGemmTile256x256); };
     const uint64_t programs_req = n_programs == 0 ? geom->num_cus : n_programs;
     const TileCfg* cfg = nullptr;
     if (tile_m == 0 && tile_n == 0 && tile_k == 0) {
@@ -602,6 +612,7 @@ ag_status_t ag_plan_gemm_all_gather(const ag_heap_geometry_t* geom, int W, int r
         // ties go to the larger tile (less operand traffic per flop)
         uint64_t best = ~uint64_t{0};
         for (const TileCfg& t : kTiles) {
+            if (!available(t)) continue;
             const uint64_t tiles = ceil_div(M_local > 0 ? M_local : 1, t.tm) * ceil_div(N, t.tn);
             const uint64_t cost = ceil_div(tiles, programs_req) * static_cast<uint64_t>(t.tm) * t.tn;
             if (cost < best) {
@@ -616,6 +627,8 @@ ag_status_t ag_plan_gemm_all_gather(const ag_heap_geometry_t* geom, int W, int r
             return fail(AG_ERR_UNSUPPORTED,
                         "tile %dx%dx%d: supported are 256x256x64, 256x224x64 and 128x128x64 (0,0,0 = choose)",
                         tile_m, tile_n, tile_k);
+        if (!available(*cfg))
+            return fail(AG_ERR_UNSUPPORTED, "tile 256x256x64 takes B K-contiguous only; use 256x224x64 or 128x128x64");
     }
     ag_plan_t p{};
     p.group_rank = g;
@@ -635,18 +648,20 @@ ag_status_t ag_plan_gemm_all_gather(const ag_heap_geometry_t* geom, int W, int r
     if (a_addr == 0 || b_addr == 0) return fail(AG_ERR_INVALID_ARG, "A or B is NULL");
     if (a_addr % 16 != 0 || b_addr % 16 != 0) return fail(AG_ERR_UNSUPPORTED, "A and B must be 16-byte aligned");
     const uint64_t a_bytes = (static_cast<uint64_t>(M_local - 1) * lda + K) * 2;
-    const uint64_t b_bytes = (static_cast<uint64_t>(N - 1) * ldb + K) * 2;
+    const uint64_t b_bytes = bt ? (static_cast<uint64_t>(K - 1) * ldb + N) * 2 : (static_cast<uint64_t>(N - 1) * ldb + K) * 2;
     for (int j = 0; j < W; ++j) {
         const uint64_t region = geom->slab_addr + static_cast<uint64_t>(rank_start + j * rank_stride) * geom->bytes_per_rank;
         if (overlaps(a_addr, a_bytes, region + out_offset, W * blk) ||
             overlaps(b_addr, b_bytes, region + out_offset, W * blk))
             return fail(AG_ERR_INVALID_ARG, "A or B overlaps the output block of region %d", rank_start + j * rank_stride);
     }
-    // per-tile buffer descriptors address at most one tile of rows with 32-bit offsets
+    // per-tile buffer descriptors address at most one tile of rows with 32-bit offsets (an N-contiguous B:
+    // one K stage of 64 rows, plus the tile's columns)
     if (static_cast<uint64_t>(cfg->tm) * lda * 2 >= (uint64_t{1} << 31) ||
-        static_cast<uint64_t>(cfg->tn) * ldb * 2 >= (uint64_t{1} << 31) ||
+        (!bt && static_cast<uint64_t>(cfg->tn) * ldb * 2 >= (uint64_t{1} << 31)) ||
+        (bt && (uint64_t{64} * ldb + cfg->tn) * 2 >= (uint64_t{1} << 31)) ||
         static_cast<uint64_t>(cfg->tm) * row_bytes >= (uint64_t{1} << 31))
-        return fail(AG_ERR_UNSUPPORTED, "a tile of rows spans 2 GiB or more");
+        return fail(AG_ERR_UNSUPPORTED, "a tile of rows (or a K stage of an N-contiguous B) spans 2 GiB or more");
     const uint64_t tiles_m = ceil_div(M_local, cfg->tm);
     const uint64_t tiles_n = ceil_div(N, cfg->tn);
     const uint64_t total = tiles_m * tiles_n;
@@ -661,19 +676,33 @@ ag_status_t ag_plan_gemm_all_gather(const ag_heap_geometry_t* geom, int W, int r
     return ok();
 }
 
-ag_status_t ag_gemm_all_gather(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
-                               const void* A, int64_t lda, const void* B, int64_t ldb,
-                               size_t out_offset, int64_t M_local, int64_t N, int64_t K,
-                               ag_dtype_t dtype, int tile_m, int tile_n, int tile_k,
-                               int n_programs, void* stream)
+ag_status_t gemm_options(const ag_gemm_options_t* options, bool* bt)
+{
+    ag_gemm_options_t opt{};
+    if (options) opt = *options;
+    for (int i = 0; i < 7; ++i)
+        if (opt.reserved[i] != 0) return fail(AG_ERR_INVALID_ARG, "options->reserved[%d] is not 0", i);
+    if (opt.b_layout != AG_B_K_CONTIGUOUS && opt.b_layout != AG_B_N_CONTIGUOUS)
+        return fail(AG_ERR_INVALID_ARG, "unknown b_layout %d", opt.b_layout);
+    *bt = opt.b_layout == AG_B_N_CONTIGUOUS;
+    return AG_OK;
+}
+
+ag_status_t launch_gemm_call(const ag_heap_t* heap, int W, int rank_start, int rank_stride, const void* A,
+                             int64_t lda, const void* B, int64_t ldb, size_t out_offset, int64_t M_local, int64_t N,
+                             int64_t K, ag_dtype_t dtype, int tile_m, int tile_n, int tile_k, int n_programs,
+                             const ag_gemm_options_t* options, void* stream)
 {
     if (!heap) return fail(AG_ERR_INVALID_ARG, "heap is NULL");
+    bool bt = false;
+    ag_status_t s = gemm_options(options, &bt);
+    if (s != AG_OK) return s;
     ag_heap_geometry_t geom;
     ag_heap_geometry(heap, &geom);
     ag_plan_t p;
-    ag_status_t s = ag_plan_gemm_all_gather(&geom, W, rank_start, rank_stride, reinterpret_cast<uint64_t>(A), lda,
-                                            reinterpret_cast<uint64_t>(B), ldb, out_offset, M_local, N, K, dtype,
-                                            tile_m, tile_n, tile_k, n_programs, &p);
+    s = plan_gemm(&geom, W, rank_start, rank_stride, reinterpret_cast<uint64_t>(A), lda,
+                  reinterpret_cast<uint64_t>(B), ldb, out_offset, M_local, N, K, dtype, tile_m, tile_n, tile_k,
+                  n_programs, bt, &p);
     if (s != AG_OK) return s;
     if (p.total_tiles == 0) return ok();
     ag::GemmLaunch l{};
@@ -697,10 +726,58 @@ ag_status_t ag_gemm_all_gather(const ag_heap_t* heap, int W, int rank_start, int
     l.world = W;
     l.cfg = p.variant;
     l.grid = p.n_programs;
+    l.b_n_contiguous = bt ? 1 : 0;
     const hipError_t e = ag::launch_gemm(l, static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported) return fail(AG_ERR_UNSUPPORTED, "fused GEMM kernel variant not available");
     if (e != hipSuccess) return fail_hip(e, "fused GEMM kernel launch");
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+ag_status_t ag_plan_gemm_all_gather(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
+                                    uint64_t a_addr, int64_t lda, uint64_t b_addr, int64_t ldb,
+                                    size_t out_offset, int64_t M_local, int64_t N, int64_t K,
+                                    ag_dtype_t dtype, int tile_m, int tile_n, int tile_k,
+                                    int n_programs, ag_plan_t* plan)
+{
+    return plan_gemm(geom, W, rank_start, rank_stride, a_addr, lda, b_addr, ldb, out_offset, M_local, N, K, dtype,
+                     tile_m, tile_n, tile_k, n_programs, false, plan);
+}
+
+ag_status_t ag_plan_gemm_all_gather_ex(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
+                                       uint64_t a_addr, int64_t lda, uint64_t b_addr, int64_t ldb,
+                                       size_t out_offset, int64_t M_local, int64_t N, int64_t K,
+                                       ag_dtype_t dtype, int tile_m, int tile_n, int tile_k,
+                                       int n_programs, const ag_gemm_options_t* options, ag_plan_t* plan)
+{
+    bool bt = false;
+    const ag_status_t s = gemm_options(options, &bt);
+    if (s != AG_OK) return s;
+    return plan_gemm(geom, W, rank_start, rank_stride, a_addr, lda, b_addr, ldb, out_offset, M_local, N, K, dtype,
+                     tile_m, tile_n, tile_k, n_programs, bt, plan);
+}
+
+ag_status_t ag_gemm_all_gather(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                               const void* A, int64_t lda, const void* B, int64_t ldb,
+                               size_t out_offset, int64_t M_local, int64_t N, int64_t K,
+                               ag_dtype_t dtype, int tile_m, int tile_n, int tile_k,
+                               int n_programs, void* stream)
+{
+    return launch_gemm_call(heap, W, rank_start, rank_stride, A, lda, B, ldb, out_offset, M_local, N, K, dtype,
+                            tile_m, tile_n, tile_k, n_programs, nullptr, stream);
+}
+
+ag_status_t ag_gemm_all_gather_ex(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                                  const void* A, int64_t lda, const void* B, int64_t ldb,
+                                  size_t out_offset, int64_t M_local, int64_t N, int64_t K,
+                                  ag_dtype_t dtype, int tile_m, int tile_n, int tile_k,
+                                  int n_programs, const ag_gemm_options_t* options, void* stream)
+{
+    return launch_gemm_call(heap, W, rank_start, rank_stride, A, lda, B, ldb, out_offset, M_local, N, K, dtype,
+                            tile_m, tile_n, tile_k, n_programs, options, stream);
 }
 
 }  // extern "C"

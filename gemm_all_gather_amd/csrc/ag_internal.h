@@ -50,7 +50,7 @@ hipError_t launch_copy(const CopyLaunch& l, hipStream_t stream);
 struct GemmKernelArgs {
     const uint64_t* heap_bases;
     const uint16_t* A;            // M x K, element (m,k) at A[m*lda + k]
-    const uint16_t* B;            // element (k,n) at B[n*ldb + k]
+    const uint16_t* B;            // element (k,n) at B[n*ldb + k], or B[k*ldb + n] when N-contiguous
     uint64_t rank_block_offset;   // out_offset + g*M*N*2
     int64_t lda, ldb;
     int32_t M, N, K;
@@ -67,6 +67,7 @@ struct GemmLaunch {
     int world;
     int cfg;           // GemmTile
     int grid;
+    int b_n_contiguous;   // 1: B is stored N-contiguous (row-major K x N)
 };
 
 hipError_t launch_gemm(const GemmLaunch& l, hipStream_t stream);

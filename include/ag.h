@@ -315,6 +315,38 @@ ag_status_t ag_plan_gemm_all_gather(const ag_heap_geometry_t* geom, int W, int r
                                     ag_dtype_t dtype, int tile_m, int tile_n, int tile_k,
                                     int n_programs, ag_plan_t* plan);
 
+/* Storage of B for ag_gemm_all_gather_ex. */
+typedef enum ag_b_layout {
+    AG_B_K_CONTIGUOUS = 0,  /* element (k,n) at B[n*ldb + k], ldb >= K (as ag_gemm_all_gather) */
+    AG_B_N_CONTIGUOUS = 1   /* element (k,n) at B[k*ldb + n], ldb >= N (a row-major K x N matrix) */
+} ag_b_layout_t;
+
+/* Options of ag_gemm_all_gather_ex; all-zero (or a NULL pointer) is ag_gemm_all_gather. */
+typedef struct ag_gemm_options {
+    int32_t b_layout;     /* ag_b_layout_t */
+    int32_t reserved[7];  /* must be 0 */
+} ag_gemm_options_t;
+
+/* ag_gemm_all_gather with options: the same product and stores, with B in
+ * either layout.  With AG_B_N_CONTIGUOUS, ldb >= N (multiple of 8), B
+ * 16-byte aligned, and 64 rows of B plus a tile's columns
+ * ((64*ldb + tile_n)*2 bytes) under 2 GiB (AG_ERR_UNSUPPORTED otherwise);
+ * B itself may be larger.  The tiles are 256x224x64 or
+ * 128x128x64 (0,0,0 chooses between them; 256x256x64 gives
+ * AG_ERR_UNSUPPORTED).  The kernel reads the N-contiguous stage with LDS
+ * transposing reads instead of a transpose pass. */
+ag_status_t ag_gemm_all_gather_ex(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                                  const void* A, int64_t lda, const void* B, int64_t ldb,
+                                  size_t out_offset, int64_t M_local, int64_t N, int64_t K,
+                                  ag_dtype_t dtype, int tile_m, int tile_n, int tile_k,
+                                  int n_programs, const ag_gemm_options_t* options, void* stream);
+
+ag_status_t ag_plan_gemm_all_gather_ex(const ag_heap_geometry_t* geom, int W, int rank_start, int rank_stride,
+                                       uint64_t a_addr, int64_t lda, uint64_t b_addr, int64_t ldb,
+                                       size_t out_offset, int64_t M_local, int64_t N, int64_t K,
+                                       ag_dtype_t dtype, int tile_m, int tile_n, int tile_k,
+                                       int n_programs, const ag_gemm_options_t* options, ag_plan_t* plan);
+
 /* ------------------------------------------------------------------------ */
 const char* ag_status_string(ag_status_t status);  /* static string, never NULL */
 const char* ag_last_error_message(void);           /* thread-local; "" after AG_OK */

@@ -361,3 +361,53 @@ def test_plan_all_to_all_partitioned_allows_more_vectors_per_thread():
 ])
 def test_plan_all_to_all_ex_rejects(kw, status):
     assert status_of(plan_a2a_ex, **kw)[0] == status
+
+
+# ---------------------------------------------------------------------------
+# fused GEMM with B in either layout
+# ---------------------------------------------------------------------------
+
+def gplan_ex(g=None, W=8, start=0, stride=1, a=A_ADDR, lda=8192, b=B_ADDR, ldb=3584, off=0, M=1024, N=3584,
+             K=8192, dtype="f16", tm=0, tn=0, tk=0, progs=0, layout="n"):
+    return ag.plan_gemm_all_gather_ex(g or geom(bytes_per_rank=1 << 30), W, start, stride, a, lda, b, ldb, off,
+                                      M, N, K, dtype, tm, tn, tk, progs, b_layout=layout)
+
+
+def test_gemm_plan_ex_k_layout_equals_the_plain_call():
+    assert gplan_ex(ldb=8192, layout="k").as_dict() == gplan().as_dict()
+    assert gplan_ex(M=16384, ldb=8192, layout="k").as_dict() == gplan(M=16384).as_dict()
+
+
+def test_gemm_plan_n_contiguous_tiles():
+    assert (gplan_ex().tile_m, gplan_ex().tile_n) == (128, 128)
+    p = gplan_ex(M=16384)
+    assert (p.tile_m, p.tile_n) == (256, 224) and p.total_tiles == 64 * 16
+    assert p.bytes_read == (16384 + 3584) * 8192 * 2
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ldb=3000), ag.AG_ERR_INVALID_ARG),              # ldb < N
+    (dict(ldb=3588), ag.AG_ERR_UNSUPPORTED),              # not a multiple of 8
+    (dict(M=16384, tm=256, tn=256, tk=64), ag.AG_ERR_UNSUPPORTED),   # no 256x256 kernel for this layout
+    (dict(ldb=1 << 24, N=8), ag.AG_ERR_UNSUPPORTED),      # one 64-row K stage spans 2 GiB
+    (dict(layout=5), ag.AG_ERR_INVALID_ARG),
+    (dict(b=SLAB + 512), ag.AG_ERR_INVALID_ARG),         # B inside an output block
+])
+def test_gemm_plan_n_contiguous_rejects(over, status):
+    got, msg = status_of(gplan_ex, **over)
+    assert got == status, (over, got, msg)
+
+
+def test_gemm_plan_n_contiguous_b_may_exceed_2_gib():
+    # each K stage gets its own descriptor: only 64 rows of B need 32-bit offsets
+    g = geom(bytes_per_rank=1 << 30)
+    assert status_of(gplan_ex, g=g, K=65536, lda=65536, ldb=32768, N=32768, b=SLAB + (64 << 30))[0] == ag.AG_OK
+    assert status_of(gplan_ex, g=g, ldb=(1 << 24) - 128, N=8)[0] == ag.AG_OK
+
+
+def test_gemm_plan_n_contiguous_b_extent_is_k_rows():
+    # the overlap check covers (K-1)*ldb + N elements of B: a B that ends just before an output block is fine
+    g = geom(bytes_per_rank=1 << 30)
+    b_bytes = ((8192 - 1) * 3584 + 3584) * 2
+    assert status_of(gplan_ex, g=g, b=SLAB - b_bytes)[0] == ag.AG_OK
+    assert status_of(gplan_ex, g=g, b=SLAB - b_bytes + 16)[0] == ag.AG_ERR_INVALID_ARG

@@ -160,10 +160,18 @@ def test_all_to_all_kernel_hoists_bases_and_pipelines_tiles(asm, vec, w, vpt):
     assert _meta(asm["ag_copy.hip"], sym)["scratch"] == 0
 
 
-@pytest.mark.parametrize("cfg", ["256ELi224", "256ELi256", "128ELi128"])
+# (tile, B N-contiguous): the 256x256 kernel takes B K-contiguous only
+GEMM_CFGS = [("256ELi224", "0"), ("256ELi224", "1"), ("256ELi256", "0"), ("128ELi128", "0"), ("128ELi128", "1")]
+
+
+def _gemm_pattern(dt, w, cfg, bt):
+    return rf"ag_gemm_kernelI{dt}ELi{w}ENS_8gemm_cfg3CfgILi{cfg}E\S*ELb{bt}EEEv"
+
+
+@pytest.mark.parametrize("cfg,bt", GEMM_CFGS)
 @pytest.mark.parametrize("dt", ["Lb0", "Lb1"])
-def test_gemm_kernel_structure(asm, cfg, dt):
-    sym, lines = _kernel_body(asm["ag_gemm.hip"], f"ag_gemm_kernelI{dt}ELi8ENS_8gemm_cfg3CfgILi{cfg}E")
+def test_gemm_kernel_structure(asm, cfg, bt, dt):
+    sym, lines = _kernel_body(asm["ag_gemm.hip"], _gemm_pattern(dt, "8", cfg, bt))
     first_barrier = next(i for i, ln in enumerate(lines) if ln.startswith("s_barrier"))
     # heap-base loads: all W of them before any tile or K-loop code (block layout may reorder the rest)
     assert sum(ln.startswith("s_load_dwordx2") for ln in lines[:first_barrier]) >= 8
@@ -189,6 +197,8 @@ def test_gemm_kernel_structure(asm, cfg, dt):
         seg = lines[a:b]
         assert not any(ln.startswith(("scratch_", "buffer_store", "s_waitcnt")) for ln in seg), seg[:5]
     assert any(re.match(r"buffer_load_dwordx4 .* lds", ln) for ln in lines)
+    # B fragments: 16-byte reads of a K-contiguous stage, transposing 8-byte reads of an N-contiguous one
+    assert any(ln.startswith("ds_read_b64_tr_b16") for ln in lines) == (bt == "1")
     # epilogue: the W destination stores of a tile form one straight run with no drain inside
     stores = [i for i, ln in enumerate(lines) if ln.startswith("buffer_store_dwordx4")]
     assert stores
@@ -206,37 +216,41 @@ def _vregs(tok):
 
 
 def _unguarded_fragment_uses(lines):
-    """MFMAs that read a register an LDS read may still be writing.
+    """Vector instructions that read a register an LDS read may still be writing.
 
     Walks the code in layout order (the fall-through path, which is how the
     unrolled K loop is laid out): every ds_read joins a queue of pending
     destination registers, s_waitcnt lgkmcnt(n) retires all but the newest n,
-    and an MFMA must not read any register still in the queue.  The hardware
+    and no MFMA or other vector instruction may read a register still in the
+    queue (the two halves of a transposed B fragment may be moved into place
+    before the MFMA).  The hardware
     does not interlock on LDS results, and the compiler does not count the
     fragment reads written as inline assembly, so the kernel has to wait
     explicitly.
     """
     pending, bad = [], []
     for i, ln in enumerate(lines):
-        if ln.startswith("s_waitcnt"):
+        if ln.startswith("s_branch "):   # the code after an unconditional branch is not its fall-through
+            pending = []
+        elif ln.startswith("s_waitcnt"):
             m = re.search(r"lgkmcnt\((\d+)\)", ln)
             if m:
                 del pending[:max(0, len(pending) - int(m.group(1)))]
         elif ln.startswith("ds_read"):
             pending.append(_vregs(ln.split()[1].rstrip(",")))
-        elif ln.startswith("v_mfma"):
+        elif ln.startswith("v_") and " " in ln:
             ops = [o.strip() for o in ln.split(None, 1)[1].split(",")]
-            src = _vregs(ops[1]) | _vregs(ops[2])
+            src = set().union(*(_vregs(o) for o in ops[1:])) if len(ops) > 1 else set()
             if any(p & src for p in pending):
                 bad.append((i, ln))
     return bad
 
 
-@pytest.mark.parametrize("cfg", ["256ELi224", "256ELi256", "128ELi128"])
+@pytest.mark.parametrize("cfg,bt", GEMM_CFGS)
 @pytest.mark.parametrize("dt", ["Lb0", "Lb1"])
 @pytest.mark.parametrize("w", ["1", "8"])
-def test_gemm_fragments_waited_before_mfma(asm, cfg, dt, w):
-    _, lines = _kernel_body(asm["ag_gemm.hip"], f"ag_gemm_kernelI{dt}ELi{w}ENS_8gemm_cfg3CfgILi{cfg}E")
+def test_gemm_fragments_waited_before_mfma(asm, cfg, bt, dt, w):
+    _, lines = _kernel_body(asm["ag_gemm.hip"], _gemm_pattern(dt, w, cfg, bt))
     assert any(ln.startswith("ds_read_b128") for ln in lines)
     bad = _unguarded_fragment_uses(lines)
     assert not bad, bad[:3]
