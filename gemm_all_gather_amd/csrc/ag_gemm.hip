@@ -193,22 +193,28 @@ struct Frag {
 
 // B fragment of a 16-column block from an N-contiguous stage (rows of k,
 // TN columns each): two transposing reads, k 0..3 then k 4..7 of the lane's
-// 8-row group.  ds_read_b64_tr_b16 gives lane i of each 16-lane group the
-// (i & 3)-th 16-bit element of the 8-byte chunk addressed by lane
-// 4*j + (i >> 2), for j = 0..3: with lane p addressing row (p >> 2) at
-// columns 4*(p & 3) .. +3, lane i receives column i of rows 0..3.  lo and hi
-// address the two halves; the block's column offset is the immediate.
+// 8-row group (the second 4 rows further: an immediate).  ds_read_b64_tr_b16
+// gives lane i of each 16-lane group the (i & 3)-th 16-bit element of the
+// 8-byte chunk addressed by lane 4*j + (i >> 2), for j = 0..3: with lane p
+// addressing row (p >> 2) at columns 4*(p & 3) .. +3, lane i receives column
+// i of rows 0..3.  A block is one 32-byte column pair of a row; rows with
+// bit 3 set hold their pairs swapped (Stage::bt_off), so a lane of such a row
+// finds an even logical pair one pair right and an odd one one pair left.
+// lo_even / lo_odd are the lane's addresses for blocks whose logical pair is
+// even / odd; the block's column offset is the immediate.
 template <class C>
 struct FragT {
     template <class V>
-    static __device__ __forceinline__ void read(V& dst, uint32_t lo, uint32_t hi, int block)
+    static __device__ __forceinline__ void read(V& dst, uint32_t lo_even, uint32_t lo_odd, int block)
     {
         u32x2 a, b;
-        switch (block) {   // the offset must be an immediate
+        switch (block) {   // the offsets must be immediates
 #define AG_FRAGT_CASE(n)                                                                                  \
     case n:                                                                                               \
-        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(a) : "v"(lo), "i"(n * 32));            \
-        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(b) : "v"(hi), "i"(n * 32));            \
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"                                                \
+                     : "=v"(a) : "v"((n & 1) ? lo_odd : lo_even), "i"(n * 32));                           \
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"                                                \
+                     : "=v"(b) : "v"((n & 1) ? lo_odd : lo_even), "i"(n * 32 + 4 * C::TN * 2));           \
         break;
             AG_FRAGT_CASE(0) AG_FRAGT_CASE(1) AG_FRAGT_CASE(2) AG_FRAGT_CASE(3)
             AG_FRAGT_CASE(4) AG_FRAGT_CASE(5) AG_FRAGT_CASE(6) AG_FRAGT_CASE(7)
@@ -259,14 +265,20 @@ struct Stage {
         }
     }
     // N-contiguous B: the stage is BK rows of k with TN*2 bytes each, dense in
-    // LDS; byte x of the stage region comes from row x / (TN*2), byte column
-    // x % (TN*2) of the tile's columns.  lane16 = 16 * lane.
+    // LDS; byte x of the stage region comes from row r = x / (TN*2) of the
+    // stage, byte column x % (TN*2) of the tile's columns with bit 5 flipped
+    // when bit 3 of r is set (32-byte pairs swapped; TN*2 is a multiple of
+    // 64).  The transposing reads of lanes 0..31 touch rows 0..3 and 8..11 of
+    // a K-step; with a row pitch that is a multiple of 64 bytes those rows
+    // would start on the same banks, and the swap moves rows 8..11 onto the
+    // banks rows 0..3 leave free.  lane16 = 16 * lane.
     static __device__ __forceinline__ uint32_t bt_off(int i, uint32_t lane16, uint32_t ld2)
     {
         constexpr uint32_t RB = C::TN * 2;
+        static_assert(RB % 64 == 0, "pairs are swapped within a row");
         const uint32_t x = static_cast<uint32_t>(i) * 1024u + lane16;
         const uint32_t row = x / RB;
-        return row * ld2 + (x - row * RB);
+        return row * ld2 + ((x - row * RB) ^ (((row >> 3) & 1u) << 5));
     }
     // The descriptor of N-contiguous stage kt starts at its first row: the
     // buffer range check covers the VGPR and immediate offsets but not the
@@ -364,9 +376,14 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
                                    : (static_cast<uint32_t>((i - C::A_INSTR) * C::RPI) + lrow) * ldb2 + lchunk * 16u;
     }
     // N-contiguous B fragments: lane (q = lane >> 4, p = lane & 15) addresses row 8q + (p >> 2) of its
-    // K-step, columns 4*(p & 3) .. +3 of its wave's first block
+    // K-step, columns 4*(p & 3) .. +3 of its wave's first block (logical pair wn*BN).  Rows of odd q
+    // hold their pairs swapped: block b's data sits one pair right of its place if wn*BN + b is even,
+    // one pair left if it is odd.
     const uint32_t bt_lane = static_cast<uint32_t>((8 * (lane >> 4) + ((lane & 15) >> 2)) * (C::TN * 2)) +
                              static_cast<uint32_t>(wn * C::WTN + 4 * (lane & 3)) * 2u;
+    const int bt_shift = ((lane >> 4) & 1) * (((wn * C::BN) & 1) ? -32 : 32);   // for even b
+    const uint32_t bt_even = bt_lane + static_cast<uint32_t>(bt_shift);
+    const uint32_t bt_odd = bt_lane - static_cast<uint32_t>(bt_shift);
     // fragment of MFMA K-step kk: row (lane & 15) of a 16-row block, logical chunk kk*4 + (lane >> 4)
     uint32_t frag_off[C::KSUB];
 #pragma unroll
@@ -439,10 +456,10 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
 #pragma unroll
             for (int bm = 0; bm < C::BM; ++bm) Frag<C>::read(fa[f][bm], sa, bm);
             if constexpr (BT) {
-                const uint32_t lo = sbase + C::A_BYTES + bt_lane + static_cast<uint32_t>(kk * 32 * C::TN * 2);
-                const uint32_t hi = lo + static_cast<uint32_t>(4 * C::TN * 2);
+                const uint32_t kb = sbase + C::A_BYTES + static_cast<uint32_t>(kk * 32 * C::TN * 2);
+                const uint32_t le = kb + bt_even, lo = kb + bt_odd;
 #pragma unroll
-                for (int bn = 0; bn < C::BN; ++bn) FragT<C>::read(fb[f][bn], lo, hi, bn);
+                for (int bn = 0; bn < C::BN; ++bn) FragT<C>::read(fb[f][bn], le, lo, bn);
             } else {
 #pragma unroll
                 for (int bn = 0; bn < C::BN; ++bn) Frag<C>::read(fb[f][bn], sb, bn);

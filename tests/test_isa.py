@@ -279,14 +279,15 @@ def test_report_registers(asm, capsys):
     assert rows
     # the instantiations the benchmark workloads run, then a summary over all of them
     bench = [r"ag_copy_kernelILi16ELi8ELi1ELi0ELb0E", r"ag_a2a_kernelILi16ELi8ELi1E",
-             r"ag_gemm_kernelILb0ELi8E\S*CfgILi256ELi224E", r"ag_gemm_kernelILb1ELi8E\S*CfgILi256ELi224E",
-             r"ag_gemm_kernelILb0ELi8E\S*CfgILi128ELi128E", r"ag_gemm_kernelILb0ELi1E\S*CfgILi256ELi224E"]
+             r"ag_gemm_kernelILb0ELi8E\S*CfgILi256ELi224E\S*ELb0EEEv", r"ag_gemm_kernelILb1ELi8E\S*CfgILi256ELi224E\S*ELb0EEEv",
+             r"ag_gemm_kernelILb0ELi8E\S*CfgILi128ELi128E\S*ELb0EEEv", r"ag_gemm_kernelILb0ELi1E\S*CfgILi256ELi224E\S*ELb0EEEv",
+             r"ag_gemm_kernelILb0ELi8E\S*CfgILi256ELi224E\S*ELb1EEEv", r"ag_gemm_kernelILb0ELi8E\S*CfgILi128ELi128E\S*ELb1EEEv"]
     with capsys.disabled():
         print()
         for pat in bench:
             for sym, m in rows:
                 if re.search(pat, sym):
-                    print(f"{sym[:100]:100s} vgpr={m['vgpr']} agpr_offset={m['agpr_offset']} sgpr={m['sgpr']} "
+                    print(f"{sym[:104]:104s} vgpr={m['vgpr']} agpr_offset={m['agpr_offset']} sgpr={m['sgpr']} "
                           f"scratch={m['scratch']} lds={m['lds']}")
                     break
         print(f"{len(rows)} instantiations: max vgpr {max(m['vgpr'] for _, m in rows)}, "
