@@ -227,7 +227,8 @@ def _context(args, stream, timed, views, ins, geom):
 
 
 def _context_fused(args, stream, timed, views, fu_off):
-    """The fused workload at M_local 1024 (fp16) and at M_local 16384 in bf16, W=8, timed like the headline."""
+    """The fused workload at M_local 1024 (fp16), at M_local 16384 in bf16, and at M_local 16384 in fp16 with B
+    stored N-contiguous (a row-major K x N matrix), W=8, timed like the headline."""
     import numpy as np
     import torch
     from gemm_all_gather_amd import binding as ag
@@ -237,15 +238,19 @@ def _context_fused(args, stream, timed, views, fu_off):
     sub.steps, sub.warmup = max(5, args.steps // 10), 2
     res = {}
     region = views[0].geometry().bytes_per_rank
-    for name, M, dtype in (("M1024_f16", 1024, "f16"), ("M16384_bf16", 16384, "bf16")):
+    for name, M, dtype, layout in (("M1024_f16", 1024, "f16", "k"), ("M16384_bf16", 16384, "bf16", "k"),
+                                   ("M16384_f16_B_row_major_KxN", 16384, "f16", "n")):
         if fu_off + FU_W * M * FU_N * 2 > region:   # heap sized for a smaller --fused-m
             continue
         fa = [torch.from_numpy(gen.normal_scaled((M, FU_K), dtype, FU_K ** -0.5, 12, j).view(np.uint8)
                                .reshape(-1).copy()).cuda() for j in range(FU_W)]
-        fb = torch.from_numpy(gen.normal_scaled((FU_N, FU_K), dtype, FU_K ** -0.5, 13).view(np.uint8)
-                              .reshape(-1).copy()).cuda()
-        ms, _ = timed(lambda: [ag.gemm_all_gather(views[j], FU_W, 0, 1, fa[j], FU_K, fb, FU_K, fu_off, M, FU_N, FU_K,
-                                                  dtype, 0, 0, 0, 0, stream) for j in range(FU_W)], sub)
+        b_nk = gen.normal_scaled((FU_N, FU_K), dtype, FU_K ** -0.5, 13)
+        b_host = b_nk if layout == "k" else np.ascontiguousarray(b_nk.T)
+        ldb = FU_K if layout == "k" else FU_N
+        fb = torch.from_numpy(b_host.view(np.uint8).reshape(-1).copy()).cuda()
+        ms, _ = timed(lambda: [ag.gemm_all_gather_ex(views[j], FU_W, 0, 1, fa[j], FU_K, fb, ldb, fu_off, M, FU_N,
+                                                     FU_K, dtype, 0, 0, 0, 0, b_layout=layout, stream=stream)
+                               for j in range(FU_W)], sub)
         flops = 2.0 * M * FU_N * FU_K
         tf = FU_W * flops / (ms / 1e3) / 1e12
         res[name] = {"TFLOPs": round(tf, 1), "frac_of_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
