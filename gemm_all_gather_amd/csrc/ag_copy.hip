@@ -50,12 +50,26 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// Cache-policy bits of the destination stores.  Non-temporal (nt, bit 1):
-// the W written copies are not re-read by this kernel, and streaming them
-// measured ~40% faster than the default policy on a 75 MB/call workload and
-// equal on a 2.4 GB/call one.
+// Cache-policy bits of the destination stores.  The W written copies are not
+// re-read by these kernels, so they are streamed: non-temporal (nt, bit 1),
+// about twice as fast as the default policy (or sc1 alone) on a 75 MB/call
+// workload.  Launches on at least half the CUs whose stores are never waited
+// for use nt with system coherence scope (sc1, bit 4): 1.5-2% faster again
+// (6.54 against 6.43 TB/s at W=8, 1024x4096 fp16, 128 programs; 458 against
+// 466-473 us at 16384x8192).  Those stores take longer to retire, so kernels
+// that wait on them (destination groups: 3.1 against 5.0 TB/s with groups of
+// one) or with few programs (64: 4.4 against 4.9 TB/s) keep nt alone.  nt with
+// sc0 equals nt alone.
 #ifndef AG_COPY_STORE_AUX
 #define AG_COPY_STORE_AUX 2
+#endif
+#ifndef AG_COPY_STORE_AUX_WIDE
+#define AG_COPY_STORE_AUX_WIDE 18
+#endif
+// Cache-policy bits of the input loads (each input byte is read once):
+// default.  Non-temporal loads measured 1.8x slower on the 1024x4096 workload.
+#ifndef AG_COPY_LOAD_AUX
+#define AG_COPY_LOAD_AUX 0
 #endif
 
 // Word 3 of a raw (stride 0) buffer descriptor on gfx9-family parts:
@@ -82,23 +96,27 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(uint64_t base, uint32_t num_r
 template <int VEC> struct Vec;
 template <> struct Vec<16> {
     using T = u32x4;
-    static __device__ T load(__amdgpu_buffer_rsrc_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0); }
-    static __device__ void store(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) { __builtin_amdgcn_raw_buffer_store_b128(v, r, o, 0, AG_COPY_STORE_AUX); }
+    static __device__ T load(__amdgpu_buffer_rsrc_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, AG_COPY_LOAD_AUX); }
+    template <int AUX>
+    static __device__ void store(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) { __builtin_amdgcn_raw_buffer_store_b128(v, r, o, 0, AUX); }
 };
 template <> struct Vec<8> {
     using T = u32x2;
-    static __device__ T load(__amdgpu_buffer_rsrc_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0); }
-    static __device__ void store(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) { __builtin_amdgcn_raw_buffer_store_b64(v, r, o, 0, AG_COPY_STORE_AUX); }
+    static __device__ T load(__amdgpu_buffer_rsrc_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, AG_COPY_LOAD_AUX); }
+    template <int AUX>
+    static __device__ void store(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) { __builtin_amdgcn_raw_buffer_store_b64(v, r, o, 0, AUX); }
 };
 template <> struct Vec<4> {
     using T = unsigned int;
-    static __device__ T load(__amdgpu_buffer_rsrc_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0); }
-    static __device__ void store(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) { __builtin_amdgcn_raw_buffer_store_b32(v, r, o, 0, AG_COPY_STORE_AUX); }
+    static __device__ T load(__amdgpu_buffer_rsrc_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, AG_COPY_LOAD_AUX); }
+    template <int AUX>
+    static __device__ void store(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) { __builtin_amdgcn_raw_buffer_store_b32(v, r, o, 0, AUX); }
 };
 template <> struct Vec<2> {
     using T = unsigned short;
-    static __device__ T load(__amdgpu_buffer_rsrc_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b16(r, o, 0, 0); }
-    static __device__ void store(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) { __builtin_amdgcn_raw_buffer_store_b16(v, r, o, 0, AG_COPY_STORE_AUX); }
+    static __device__ T load(__amdgpu_buffer_rsrc_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b16(r, o, 0, AG_COPY_LOAD_AUX); }
+    template <int AUX>
+    static __device__ void store(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) { __builtin_amdgcn_raw_buffer_store_b16(v, r, o, 0, AUX); }
 };
 
 struct TileRef {
@@ -111,10 +129,13 @@ struct TileRef {
 // W destinations per tile; G destinations per wait (0: none).  PART: the
 // partitioned schedule (W = 1, the group size is a.world at run time).  A
 // partitioned program of the all-to-all (a.chunk_bytes > 0) reads the chunk
-// its destination receives: chunk (g + i) mod W for destination i.
-template <int VEC, int W, int VPT, int G, bool PART>
+// its destination receives: chunk (g + i) mod W for destination i.  WIDE: the
+// stores' cache policy for launches on at least half the CUs (never with G).
+template <int VEC, int W, int VPT, int G, bool PART, bool WIDE>
 __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
 {
+    constexpr int kAux = WIDE ? AG_COPY_STORE_AUX_WIDE : AG_COPY_STORE_AUX;
+    static_assert(!WIDE || G == 0, "waited-for stores keep the plain streaming policy");
     using VT = Vec<VEC>;
     using V = typename VT::T;
     static_assert(G == 0 || G < W, "a group smaller than the destination count");
@@ -228,7 +249,7 @@ __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
         for (int i = 0; i < W; ++i) {   // local region first, then the rotated peers
             const __amdgpu_buffer_rsrc_t dst = make_rsrc(dest[i] + r.off, r.records);
 #pragma unroll
-            for (int j = 0; j < VPT; ++j) VT::store(v[j], dst, vo[j]);
+            for (int j = 0; j < VPT; ++j) VT::template store<kAux>(v[j], dst, vo[j]);
             // end of a destination group: retire everything issued before it
             if (G > 0 && (i + 1) % G == 0 && i + 1 < W) wait_vmcnt<G * VPT>();
         }
@@ -267,12 +288,14 @@ __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
 // All-to-all: tile t of every input chunk is loaded (chunk (g + i) mod W
 // for destination i), then tile t of destination i's block receives it,
 // local region first, then the rotated peers.  The W chunk tiles of the next
-// tile are loaded before the current ones are stored.
-template <int VEC, int W, int VPT>
+// tile are loaded before the current ones are stored.  WIDE: as for the
+// all-gather kernel.
+template <int VEC, int W, int VPT, bool WIDE>
 __global__ __launch_bounds__(256) void ag_a2a_kernel(CopyKernelArgs a)
 {
     using VT = Vec<VEC>;
     using V = typename VT::T;
+    constexpr int kAux = WIDE ? AG_COPY_STORE_AUX_WIDE : AG_COPY_STORE_AUX;
 
     uint64_t src[W];    // input chunk meant for destination i = group member (g + i) mod W
 #pragma unroll
@@ -365,7 +388,7 @@ __global__ __launch_bounds__(256) void ag_a2a_kernel(CopyKernelArgs a)
         for (int i = 0; i < W; ++i) {   // local region first, then the rotated peers
             const __amdgpu_buffer_rsrc_t d = make_rsrc(dest[i] + r.off, r.records);
 #pragma unroll
-            for (int j = 0; j < VPT; ++j) VT::store(v[i][j], d, vo[j]);
+            for (int j = 0; j < VPT; ++j) VT::template store<kAux>(v[i][j], d, vo[j]);
         }
     };
     store_tile(ta, oa, va);
@@ -398,45 +421,46 @@ using CopyFn = void (*)(CopyKernelArgs);
 // 16- and 8-byte vectors (G < W)
 // (the partitioned schedule: W = 1, G = 0, PART)
 template <int VEC, int W, int VPT>
-CopyFn pick_group(int g, bool part)
+CopyFn pick_group(int g, bool part, bool wide)
 {
     if (part) {
-        if constexpr (W == 1) return g == 0 ? ag_copy_kernel<VEC, 1, VPT, 0, true> : nullptr;
+        if constexpr (W == 1)
+            if (g == 0) return wide ? ag_copy_kernel<VEC, 1, VPT, 0, true, true> : ag_copy_kernel<VEC, 1, VPT, 0, true, false>;
         return nullptr;
     }
-    if (g == 0) return ag_copy_kernel<VEC, W, VPT, 0, false>;
+    if (g == 0) return wide ? ag_copy_kernel<VEC, W, VPT, 0, false, true> : ag_copy_kernel<VEC, W, VPT, 0, false, false>;
     if constexpr (VEC >= 8) {
-        if constexpr (W > 1) if (g == 1) return ag_copy_kernel<VEC, W, VPT, 1, false>;
-        if constexpr (W > 2) if (g == 2) return ag_copy_kernel<VEC, W, VPT, 2, false>;
-        if constexpr (W > 4) if (g == 4) return ag_copy_kernel<VEC, W, VPT, 4, false>;
+        if constexpr (W > 1) if (g == 1) return ag_copy_kernel<VEC, W, VPT, 1, false, false>;
+        if constexpr (W > 2) if (g == 2) return ag_copy_kernel<VEC, W, VPT, 2, false, false>;
+        if constexpr (W > 4) if (g == 4) return ag_copy_kernel<VEC, W, VPT, 4, false, false>;
     }
     return nullptr;
 }
 
 template <int VEC, int W>
-CopyFn pick_vpt(int vpt, int g, bool part)
+CopyFn pick_vpt(int vpt, int g, bool part, bool wide)
 {
     switch (vpt) {
-    case 1: return pick_group<VEC, W, 1>(g, part);
-    case 2: return pick_group<VEC, W, 2>(g, part);
-    case 4: return pick_group<VEC, W, 4>(g, part);
-    case 8: return pick_group<VEC, W, 8>(g, part);
+    case 1: return pick_group<VEC, W, 1>(g, part, wide);
+    case 2: return pick_group<VEC, W, 2>(g, part, wide);
+    case 4: return pick_group<VEC, W, 4>(g, part, wide);
+    case 8: return pick_group<VEC, W, 8>(g, part, wide);
     default: return nullptr;
     }
 }
 
 template <int VEC>
-CopyFn pick_world(int w, int vpt, int g, bool part)
+CopyFn pick_world(int w, int vpt, int g, bool part, bool wide)
 {
     switch (w) {
-    case 1: return pick_vpt<VEC, 1>(vpt, g, part);
-    case 2: return pick_vpt<VEC, 2>(vpt, g, part);
-    case 3: return pick_vpt<VEC, 3>(vpt, g, part);
-    case 4: return pick_vpt<VEC, 4>(vpt, g, part);
-    case 5: return pick_vpt<VEC, 5>(vpt, g, part);
-    case 6: return pick_vpt<VEC, 6>(vpt, g, part);
-    case 7: return pick_vpt<VEC, 7>(vpt, g, part);
-    case 8: return pick_vpt<VEC, 8>(vpt, g, part);
+    case 1: return pick_vpt<VEC, 1>(vpt, g, part, wide);
+    case 2: return pick_vpt<VEC, 2>(vpt, g, part, wide);
+    case 3: return pick_vpt<VEC, 3>(vpt, g, part, wide);
+    case 4: return pick_vpt<VEC, 4>(vpt, g, part, wide);
+    case 5: return pick_vpt<VEC, 5>(vpt, g, part, wide);
+    case 6: return pick_vpt<VEC, 6>(vpt, g, part, wide);
+    case 7: return pick_vpt<VEC, 7>(vpt, g, part, wide);
+    case 8: return pick_vpt<VEC, 8>(vpt, g, part, wide);
     default: return nullptr;
     }
 }
@@ -444,51 +468,51 @@ CopyFn pick_world(int w, int vpt, int g, bool part)
 // ---- all-to-all instantiations: VEC x W x VPT with VEC*VPT <= 32 bytes per
 // thread and chunk tile (two register sets of W such tiles stay live)
 template <int VEC, int W>
-CopyFn pick_a2a_vpt(int vpt)
+CopyFn pick_a2a_vpt(int vpt, bool wide)
 {
     switch (vpt) {
-    case 1: return ag_a2a_kernel<VEC, W, 1>;
-    case 2: return ag_a2a_kernel<VEC, W, 2>;
-    case 4: if constexpr (VEC * 4 <= 32) return ag_a2a_kernel<VEC, W, 4>; else return nullptr;
-    case 8: if constexpr (VEC * 8 <= 32) return ag_a2a_kernel<VEC, W, 8>; else return nullptr;
+    case 1: return wide ? ag_a2a_kernel<VEC, W, 1, true> : ag_a2a_kernel<VEC, W, 1, false>;
+    case 2: return wide ? ag_a2a_kernel<VEC, W, 2, true> : ag_a2a_kernel<VEC, W, 2, false>;
+    case 4: if constexpr (VEC * 4 <= 32) return wide ? ag_a2a_kernel<VEC, W, 4, true> : ag_a2a_kernel<VEC, W, 4, false>; else return nullptr;
+    case 8: if constexpr (VEC * 8 <= 32) return wide ? ag_a2a_kernel<VEC, W, 8, true> : ag_a2a_kernel<VEC, W, 8, false>; else return nullptr;
     default: return nullptr;
     }
 }
 
 template <int VEC>
-CopyFn pick_a2a_world(int w, int vpt)
+CopyFn pick_a2a_world(int w, int vpt, bool wide)
 {
     switch (w) {
-    case 1: return pick_a2a_vpt<VEC, 1>(vpt);
-    case 2: return pick_a2a_vpt<VEC, 2>(vpt);
-    case 3: return pick_a2a_vpt<VEC, 3>(vpt);
-    case 4: return pick_a2a_vpt<VEC, 4>(vpt);
-    case 5: return pick_a2a_vpt<VEC, 5>(vpt);
-    case 6: return pick_a2a_vpt<VEC, 6>(vpt);
-    case 7: return pick_a2a_vpt<VEC, 7>(vpt);
-    case 8: return pick_a2a_vpt<VEC, 8>(vpt);
+    case 1: return pick_a2a_vpt<VEC, 1>(vpt, wide);
+    case 2: return pick_a2a_vpt<VEC, 2>(vpt, wide);
+    case 3: return pick_a2a_vpt<VEC, 3>(vpt, wide);
+    case 4: return pick_a2a_vpt<VEC, 4>(vpt, wide);
+    case 5: return pick_a2a_vpt<VEC, 5>(vpt, wide);
+    case 6: return pick_a2a_vpt<VEC, 6>(vpt, wide);
+    case 7: return pick_a2a_vpt<VEC, 7>(vpt, wide);
+    case 8: return pick_a2a_vpt<VEC, 8>(vpt, wide);
     default: return nullptr;
     }
 }
 
-CopyFn pick_kernel(int kind, int vec, int w, int g, int vpt, bool part)
+CopyFn pick_kernel(int kind, int vec, int w, int g, int vpt, bool part, bool wide)
 {
     // the partitioned all-to-all runs the partitioned copy kernel (one destination per program)
     if (kind == kCopyAllToAll && !part) {
         if (g != 0) return nullptr;
         switch (vec) {
-        case 16: return pick_a2a_world<16>(w, vpt);
-        case 8: return pick_a2a_world<8>(w, vpt);
-        case 4: return pick_a2a_world<4>(w, vpt);
-        case 2: return pick_a2a_world<2>(w, vpt);
+        case 16: return pick_a2a_world<16>(w, vpt, wide);
+        case 8: return pick_a2a_world<8>(w, vpt, wide);
+        case 4: return pick_a2a_world<4>(w, vpt, wide);
+        case 2: return pick_a2a_world<2>(w, vpt, wide);
         default: return nullptr;
         }
     }
     switch (vec) {
-    case 16: return pick_world<16>(w, vpt, g, part);
-    case 8: return pick_world<8>(w, vpt, g, part);
-    case 4: return pick_world<4>(w, vpt, g, part);
-    case 2: return pick_world<2>(w, vpt, g, part);
+    case 16: return pick_world<16>(w, vpt, g, part, wide);
+    case 8: return pick_world<8>(w, vpt, g, part, wide);
+    case 4: return pick_world<4>(w, vpt, g, part, wide);
+    case 2: return pick_world<2>(w, vpt, g, part, wide);
     default: return nullptr;
     }
 }
@@ -497,12 +521,12 @@ CopyFn pick_kernel(int kind, int vec, int w, int g, int vpt, bool part)
 
 bool copy_supported(int kind, int vec_bytes, int dests, int group, int vpt, bool partitioned)
 {
-    return pick_kernel(kind, vec_bytes, dests, group, vpt, partitioned) != nullptr;
+    return pick_kernel(kind, vec_bytes, dests, group, vpt, partitioned, false) != nullptr;
 }
 
 hipError_t launch_copy(const CopyLaunch& l, hipStream_t stream)
 {
-    CopyFn fn = pick_kernel(l.kind, l.vec_bytes, l.dests, l.group, l.vpt, l.args.partitioned != 0);
+    CopyFn fn = pick_kernel(l.kind, l.vec_bytes, l.dests, l.group, l.vpt, l.args.partitioned != 0, l.wide != 0);
     const uint32_t max_slices = l.kind == kCopyAllToAll ? 1 : 4;
     if (fn == nullptr || l.args.slices < 1 || l.args.slices > max_slices || l.grid < 1 || l.args.world < 1)
         return hipErrorInvalidValue;

@@ -478,6 +478,8 @@ ag_status_t launch_copy_call(const ag_heap_t* heap, int kind, int W, int rank_st
     l.group = p.dest_group;
     l.vpt = p.vectors_per_thread;
     l.grid = p.n_programs;
+    // streaming stores with system scope on wide launches whose stores are never waited for
+    l.wide = (p.dest_group == 0 && 2 * static_cast<int64_t>(p.n_programs) >= geom.num_cus) ? 1 : 0;
     const hipError_t e2 = ag::launch_copy(l, static_cast<hipStream_t>(stream));
     if (e2 != hipSuccess) return fail_hip(e2, kind == ag::kCopyAllToAll ? "all-to-all kernel launch" : "all-gather kernel launch");
     return ok();

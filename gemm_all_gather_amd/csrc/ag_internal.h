@@ -40,6 +40,7 @@ struct CopyLaunch {
     int group;         // destinations per wait (0 = no waits between destinations)
     int vpt;           // vector accesses per thread per tile
     int grid;          // workgroups
+    int wide;          // 1: the store policy of launches on at least half the CUs (no destination groups)
 };
 
 // Whether the launcher has a kernel for (kind, vec, dests, group, vpt, schedule) (host-only).
