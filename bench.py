@@ -240,7 +240,17 @@ def _context_fused(args, stream, timed, views, fu_off):
     region = views[0].geometry().bytes_per_rank
     for name, M, dtype, layout in (("M1024_f16", 1024, "f16", "k"), ("M16384_bf16", 16384, "bf16", "k"),
                                    ("M16384_f16_B_row_major_KxN", 16384, "f16", "n")):
-        if fu_off + FU_W * M * FU_N * 2 > region:   # heap sized for a smaller --fused-m
+        own = None
+        if M != FU_M:
+            # a heap of its own, regions sized for this workload's gathered output, as for the
+            # all-gather workloads (the region stride moves the store rate)
+            S = -(-(FU_W * M * FU_N * 2) // (2 << 20)) * (2 << 20)
+            own_slab = torch.zeros(FU_W * S, dtype=torch.uint8, device="cuda")
+            own = ag.Heap.wrap(own_slab, FU_W, S)
+            vws, off = [own.view(r) for r in range(FU_W)], 0
+        else:
+            vws, off = views, fu_off
+        if off + FU_W * M * FU_N * 2 > (region if own is None else S):
             continue
         fa = [torch.from_numpy(gen.normal_scaled((M, FU_K), dtype, FU_K ** -0.5, 12, j).view(np.uint8)
                                .reshape(-1).copy()).cuda() for j in range(FU_W)]
@@ -248,7 +258,7 @@ def _context_fused(args, stream, timed, views, fu_off):
         b_host = b_nk if layout == "k" else np.ascontiguousarray(b_nk.T)
         ldb = FU_K if layout == "k" else FU_N
         fb = torch.from_numpy(b_host.view(np.uint8).reshape(-1).copy()).cuda()
-        ms, _ = timed(lambda: [ag.gemm_all_gather_ex(views[j], FU_W, 0, 1, fa[j], FU_K, fb, ldb, fu_off, M, FU_N,
+        ms, _ = timed(lambda: [ag.gemm_all_gather_ex(vws[j], FU_W, 0, 1, fa[j], FU_K, fb, ldb, off, M, FU_N,
                                                      FU_K, dtype, 0, 0, 0, 0, b_layout=layout, stream=stream)
                                for j in range(FU_W)], sub)
         flops = 2.0 * M * FU_N * FU_K
@@ -256,6 +266,12 @@ def _context_fused(args, stream, timed, views, fu_off):
         res[name] = {"TFLOPs": round(tf, 1), "frac_of_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                      "us_per_call": round(ms * 1e3 / FU_W, 1)}
         del fa, fb
+        if own is not None:
+            torch.cuda.synchronize()
+            for v in vws:
+                v.destroy()
+            own.destroy()
+            del own_slab
         torch.cuda.empty_cache()
     return res
 
