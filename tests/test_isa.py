@@ -124,6 +124,27 @@ def test_copy_kernel_hoists_bases_and_never_drains_before_a_store(asm, vec, w, v
     assert meta["scratch"] == 0, meta
 
 
+@pytest.mark.parametrize("kernel", ["ag_copy_kernelILi16ELi8ELi1ELi0ELb0E", "ag_copy_kernelILi8ELi4ELi2ELi0ELb0E",
+                                    "ag_copy_kernelILi16ELi1ELi1ELi0ELb1E", "ag_a2a_kernelILi16ELi8ELi2E"])
+def test_copy_store_policy(asm, kernel):
+    """Destination stores stream (nt); the wide variant (launches on at least half the CUs, never
+    waited for) adds system scope (sc1), the other keeps nt alone."""
+    for wide, want in (("0", {"nt"}), ("1", {"sc1", "nt"})):
+        _, lines = _kernel_body(asm["ag_copy.hip"], f"{kernel}Lb{wide}E")
+        stores = [ln for ln in lines if ln.startswith("buffer_store")]
+        assert stores
+        for ln in stores:
+            bits = set(ln.split()) & {"sc0", "sc1", "nt"}
+            assert bits == want, (wide, ln)
+
+
+def test_grouped_copy_kernels_keep_plain_streaming_stores(asm):
+    _, lines = _kernel_body(asm["ag_copy.hip"], "ag_copy_kernelILi16ELi8ELi1ELi2ELb0ELb0E")
+    stores = [ln for ln in lines if ln.startswith("buffer_store")]
+    assert stores and all((set(ln.split()) & {"sc0", "sc1", "nt"}) == {"nt"} for ln in stores)
+    assert not re.search(r"ag_copy_kernelILi16ELi8ELi1ELi2ELb0ELb1E", asm["ag_copy.hip"]), "no wide grouped kernel"
+
+
 @pytest.mark.parametrize("w,g", [(8, 1), (8, 2), (8, 4), (3, 2), (5, 4)])
 def test_grouped_copy_waits_once_per_destination_group(asm, w, g):
     """dest_group G: after every G destinations' stores one wait retires what precedes them
