@@ -20,12 +20,15 @@
 //   * 16-byte vector accesses when N*e, the input and the output block are
 //     16-byte aligned (8/4/2 otherwise);
 //   * the per-lane byte offsets inside a tile do not depend on the tile, so
-//     they are computed once; each tile only adds a uniform (scalar) base,
-//     which lets the compiler use global_load/global_store with an SGPR base
-//     and a 32-bit VGPR offset;
+//     they are computed once; each tile only rebases buffer descriptors
+//     (scalar registers), and every access is a buffer load or store with a
+//     32-bit VGPR offset, bounds-checked by the descriptor;
 //   * the next tile's loads are issued before the current tile's stores, so
 //     waiting for them never waits for the stores (the memory counter is in
-//     issue order), and no destination store is preceded by a full drain.
+//     issue order), and no destination store is preceded by a full drain;
+//   * the destination stores stream (non-temporal), with system coherence
+//     scope added on launches over at least half the CUs whose stores are
+//     never waited for (the WIDE kernels).
 //
 // Variants (ROCm/iris #594, "Reviewer performance evaluation" and "Compiler
 // inspection and grouping"; ROCm/iris #591, "INLINE grouping"; ROCm/iris
