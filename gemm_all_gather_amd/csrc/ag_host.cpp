@@ -126,6 +126,18 @@ ag_status_t finish_heap(std::shared_ptr<HeapCore> core, ag_heap_t** out)
     return ok();
 }
 
+// Launches run on the current HIP device; the heap's slab and base table
+// live on the device that was current when it was created or wrapped.
+ag_status_t check_device(const ag_heap_t* heap)
+{
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    if (dev != heap->core->device)
+        return fail(AG_ERR_INVALID_ARG, "the heap lives on device %d but device %d is current", heap->core->device, dev);
+    return AG_OK;
+}
+
 ag_status_t check_geometry(const ag_heap_geometry_t* g)
 {
     if (!g) return fail(AG_ERR_INVALID_ARG, "geometry is NULL");
@@ -217,6 +229,36 @@ ag_status_t ag_heap_wrap(void* dev_slab, int n_ranks, size_t bytes_per_rank, ag_
     if (n_ranks < 1 || n_ranks > 1024) return fail(AG_ERR_INVALID_ARG, "n_ranks %d not in [1, 1024]", n_ranks);
     if (bytes_per_rank == 0 || bytes_per_rank % 256 != 0)
         return fail(AG_ERR_INVALID_ARG, "bytes_per_rank %zu is not a positive multiple of 256", bytes_per_rank);
+    if (bytes_per_rank > (uint64_t{1} << 50) / static_cast<uint64_t>(n_ranks))
+        return fail(AG_ERR_INVALID_ARG, "heap size overflows");
+    // The slab must be device memory of the current device, and the n_ranks regions must lie inside
+    // its allocation: a kernel would otherwise fault on the first launch.
+    {
+        hipPointerAttribute_t attr{};
+        hipError_t e = hipPointerGetAttributes(&attr, dev_slab);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();   // a failed query must not surface as a later launch error
+            return fail(AG_ERR_INVALID_ARG, "dev_slab is not device memory known to HIP (%s)", hipGetErrorString(e));
+        }
+        int dev = -1;
+        e = hipGetDevice(&dev);
+        if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+        if ((attr.type != hipMemoryTypeDevice && !attr.isManaged) || attr.device != dev)
+            return fail(AG_ERR_INVALID_ARG, "dev_slab is not device memory of the current device %d", dev);
+        void* base = nullptr;
+        size_t size = 0;
+        e = hipMemGetAddressRange(reinterpret_cast<hipDeviceptr_t*>(&base), &size, dev_slab);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(AG_ERR_INVALID_ARG, "the allocation holding dev_slab is unknown (%s)", hipGetErrorString(e));
+        }
+        const uint64_t need = static_cast<uint64_t>(n_ranks) * bytes_per_rank;
+        const uint64_t avail = reinterpret_cast<uint64_t>(base) + size - reinterpret_cast<uint64_t>(dev_slab);
+        if (need > avail)
+            return fail(AG_ERR_INVALID_ARG, "%d regions of %zu bytes need %llu bytes, the allocation holds %llu from dev_slab",
+                        n_ranks, bytes_per_rank, static_cast<unsigned long long>(need),
+                        static_cast<unsigned long long>(avail));
+    }
     auto core = std::make_shared<HeapCore>();
     core->slab = dev_slab;
     core->n_ranks = n_ranks;
@@ -451,6 +493,8 @@ ag_status_t launch_copy_call(const ag_heap_t* heap, int kind, int W, int rank_st
                               M, N, dtype, tile_m, tile_n, n_programs, options, &p);
     if (s != AG_OK) return s;
     if (p.total_tiles == 0) return ok();
+    s = check_device(heap);
+    if (s != AG_OK) return s;
     const int e = elem_bytes(dtype);
     const bool part = p.schedule == AG_SCHEDULE_PARTITIONED;
     ag::CopyLaunch l{};
@@ -707,6 +751,8 @@ ag_status_t launch_gemm_call(const ag_heap_t* heap, int W, int rank_start, int r
                   n_programs, bt, &p);
     if (s != AG_OK) return s;
     if (p.total_tiles == 0) return ok();
+    s = check_device(heap);
+    if (s != AG_OK) return s;
     ag::GemmLaunch l{};
     l.args.heap_bases = heap->core->table;
     l.args.A = static_cast<const uint16_t*>(A);

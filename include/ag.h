@@ -29,7 +29,9 @@
  *    ag_last_error_message() gives a one-line reason (thread-local).
  *  - Launching entry points are asynchronous and ordered on the given
  *    hipStream_t (NULL = the null stream).  They never synchronise.  A launch
- *    failure reported by the runtime returns AG_ERR_HIP.
+ *    failure reported by the runtime returns AG_ERR_HIP.  They launch on the
+ *    current HIP device, which must be the device the heap was created or
+ *    wrapped on (AG_ERR_INVALID_ARG otherwise).
  *  - Argument validation is done on the host before any HIP call; values are
  *    never remapped: 0 means "documented default", anything else is used as
  *    given or rejected.
@@ -127,9 +129,12 @@ ag_status_t ag_heap_create(int n_ranks, size_t bytes_per_rank, ag_heap_t** out);
 
 /* Build a heap over caller-owned device memory of n_ranks*bytes_per_rank
  * bytes (e.g. a torch uint8 tensor).  dev_slab must be 256-byte aligned and
- * bytes_per_rank a non-zero multiple of 256.  The library allocates and owns
- * only the base table; the caller keeps the slab alive until every handle
- * on it is destroyed. */
+ * bytes_per_rank a non-zero multiple of 256.  dev_slab must be device (or
+ * managed) memory of the current device, and its allocation must hold the
+ * n_ranks*bytes_per_rank bytes from dev_slab on (AG_ERR_INVALID_ARG
+ * otherwise: checked with hipPointerGetAttributes and hipMemGetAddressRange).
+ * The library allocates and owns only the base table; the caller keeps the
+ * slab alive until every handle on it is destroyed. */
 ag_status_t ag_heap_wrap(void* dev_slab, int n_ranks, size_t bytes_per_rank, ag_heap_t** out);
 
 /* A handle for one calling rank ("the caller's rank", as the context object

@@ -204,6 +204,38 @@ def test_library_owned_heap_create_and_alloc():
         heap.destroy()
 
 
+def test_wrap_rejects_host_memory_and_short_slabs():
+    require_gpu()
+    log("ag_heap_wrap validation: host memory, a slab shorter than its regions")
+    host = np.zeros(1 << 20, dtype=np.uint8)
+    with pytest.raises(ag.AgError) as ei:
+        ag.Heap.wrap(host.ctypes.data, 4, 256 << 10)
+    assert ei.value.status == ag.AG_ERR_INVALID_ARG
+    # a dedicated allocation of 2 MiB (the library's slab of one 2 MiB region) cannot hold 4 regions of 1 MiB
+    buf = ag.Heap.create(1, 2 << 20)
+    try:
+        slab = buf.geometry().slab_addr
+        with pytest.raises(ag.AgError) as ei:
+            ag.Heap.wrap(slab, 4, 1 << 20)
+        assert ei.value.status == ag.AG_ERR_INVALID_ARG and "allocation" in ei.value.message
+        with pytest.raises(ag.AgError):
+            ag.Heap.wrap(slab + (1 << 20), 2, 1 << 20)        # runs 1 MiB past the end
+        h = ag.Heap.wrap(slab, 2, 1 << 20)                    # exactly the allocation
+        h.destroy()
+        h = ag.Heap.wrap(slab + (1 << 20), 1, 1 << 20)        # its second half
+        h.destroy()
+    finally:
+        buf.destroy()
+    # the failed queries leave no error behind for the next launch
+    th = TorchHeap(2, 1 << 20)
+    try:
+        x = to_device(gen.uniform_pm1((16, 256), "f16", 3))
+        ag.all_gather(th.view(0), 2, 0, 1, x, 0, 16, 256, "f16")
+        torch.cuda.synchronize()
+    finally:
+        th.close()
+
+
 def test_launching_entry_point_rejects_invalid_arguments():
     require_gpu()
     log("ag_all_gather validation on the launching entry point")
