@@ -348,6 +348,36 @@ ag_status_t ag_heap_geometry(const ag_heap_t* heap, ag_heap_geometry_t* geom)
 
 namespace {
 
+// The rows the copy kernels walk.  A block (this rank's input, or one all-to-
+// all chunk, and its place in every output block) is M rows of N elements
+// with ld = N, so its M*N*e bytes are contiguous and any rows x cols = M x N
+// addresses the same bytes in the same order.  When N*e is not a multiple of
+// 16 bytes but the block's size, the input and the output block are, the
+// kernels walk rows of cols elements instead, cols*e a multiple of 16 (the
+// divisor of the block's 16-byte vector count nearest N*e/16, searched within
+// 4096 vectors of it), so that they move 16-byte vectors.  Every destination
+// receives the same bytes; only the grouping of bytes into tiles differs.
+void copy_rows(uint64_t M, uint64_t N, int e, uint64_t input_addr, uint64_t out_addr, uint64_t* rows, uint64_t* cols)
+{
+    *rows = M;
+    *cols = N;
+    const uint64_t row_bytes = N * static_cast<uint64_t>(e);
+    const uint64_t bytes = M * row_bytes;
+    if (M < 2 || row_bytes % 16 == 0 || bytes % 16 != 0 || input_addr % 16 != 0 || out_addr % 16 != 0) return;
+    const uint64_t q = bytes / 16;                                  // 16-byte vectors in the block
+    const uint64_t t = std::max<uint64_t>(1, row_bytes / 16);
+    for (uint64_t dist = 0; dist <= 4096; ++dist) {
+        for (int below = 0; below < 2; ++below) {
+            if (below && (dist == 0 || dist >= t)) continue;
+            const uint64_t d = below ? t - dist : t + dist;         // vectors per row
+            if (d > q || q % d != 0 || q / d >= (uint64_t{1} << 31) || d * 16 / e >= (uint64_t{1} << 31)) continue;
+            *cols = d * 16 / static_cast<uint64_t>(e);
+            *rows = q / d;
+            return;
+        }
+    }
+}
+
 // Validation and launch decisions shared by every copy entry point.  kind:
 // ag::kCopyAllGather (M = M_local rows per rank) or ag::kCopyAllToAll (M =
 // M_chunk rows per chunk, W chunks in the input).
@@ -433,22 +463,42 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
 
     // widest vector that every row start, the input and every output block allow
     const uint64_t out_addr = geom->slab_addr + p.rank_block_offset;   // same alignment in every region
-    int vec = 16;
-    while (vec > e && ((row_bytes % vec) != 0 || (input_addr % vec) != 0 || (out_addr % vec) != 0)) vec /= 2;
+    auto widest = [&](uint64_t rb) {
+        int v = 16;
+        while (v > e && ((rb % v) != 0 || (input_addr % v) != 0 || (out_addr % v) != 0)) v /= 2;
+        return v;
+    };
     const uint64_t tile_row_bytes = static_cast<uint64_t>(tile_n) * e;
-    const uint64_t tile_vecs = static_cast<uint64_t>(tile_m) * tile_row_bytes / vec;
     // the all-to-all's tile schedule holds W tiles per thread: <= 32 bytes of each
-    const int max_vpt = (a2a && !part) ? std::min(32 / vec, kCopyMaxVpt) : kCopyMaxVpt;
+    auto max_vpt_of = [&](int v) { return (a2a && !part) ? std::min(32 / v, kCopyMaxVpt) : kCopyMaxVpt; };
+    auto tile_fits = [&](int v) {
+        const uint64_t tv = static_cast<uint64_t>(tile_m) * tile_row_bytes / v;
+        return tv % 256 == 0 && tv / 256 <= static_cast<uint64_t>(max_vpt_of(v));
+    };
+    int vec = widest(row_bytes);
+    uint64_t rows = static_cast<uint64_t>(M), cols = static_cast<uint64_t>(N);
+    if (vec < 16) {   // the kernels' view of the block as rows of a multiple of 16 bytes, if the tile fits it
+        uint64_t r2 = 0, c2 = 0;
+        copy_rows(rows, cols, e, input_addr, out_addr, &r2, &c2);
+        if (c2 != cols && widest(c2 * e) == 16 && tile_fits(16)) {
+            rows = r2;
+            cols = c2;
+            vec = 16;
+        }
+    }
+    const uint64_t view_row_bytes = cols * static_cast<uint64_t>(e);
+    const uint64_t tile_vecs = static_cast<uint64_t>(tile_m) * tile_row_bytes / vec;
+    const int max_vpt = max_vpt_of(vec);
     if (tile_vecs % 256 != 0 || tile_vecs / 256 > static_cast<uint64_t>(max_vpt))
         return fail(AG_ERR_UNSUPPORTED, "tile %dx%d holds %llu %d-byte vectors; 256 to %d are supported",
                     tile_m, tile_n, static_cast<unsigned long long>(tile_vecs), vec, 256 * max_vpt);
-    if (static_cast<uint64_t>(tile_m) * row_bytes >= (uint64_t{1} << 31))
+    if (static_cast<uint64_t>(tile_m) * view_row_bytes >= (uint64_t{1} << 31))
         return fail(AG_ERR_UNSUPPORTED, "a tile spans 2 GiB or more of the input");
     if (p.dest_group > 0 && vec < 8)
         return fail(AG_ERR_UNSUPPORTED, "destination groups need 16- or 8-byte vectors (this call gets %d)", vec);
 
-    const uint64_t tiles_m = ceil_div(M, tile_m);
-    const uint64_t tiles_n = ceil_div(N, tile_n);
+    const uint64_t tiles_m = ceil_div(rows, tile_m);
+    const uint64_t tiles_n = ceil_div(cols, tile_n);
     const uint64_t total = tiles_m * tiles_n;
     if (total >= (uint64_t{1} << 31)) return fail(AG_ERR_UNSUPPORTED, "more than 2^31 tiles");
 
@@ -501,9 +551,15 @@ ag_status_t launch_copy_call(const ag_heap_t* heap, int kind, int W, int rank_st
     l.args.heap_bases = heap->core->table;
     l.args.input = static_cast<const uint8_t*>(input);
     l.args.rank_block_offset = p.rank_block_offset;
-    l.args.row_bytes = static_cast<uint64_t>(N) * e;
+    // the planner's view of the block: rows of a multiple of 16 bytes when it chose 16-byte vectors
+    // for rows that are not
+    uint64_t rows = static_cast<uint64_t>(M), cols = static_cast<uint64_t>(N);
+    if (p.vec_bytes == 16 && (static_cast<uint64_t>(N) * e) % 16 != 0)
+        copy_rows(static_cast<uint64_t>(M), static_cast<uint64_t>(N), e, reinterpret_cast<uint64_t>(input),
+                  geom.slab_addr + p.rank_block_offset, &rows, &cols);
+    l.args.row_bytes = cols * static_cast<uint64_t>(e);
     l.args.chunk_bytes = kind == ag::kCopyAllToAll ? static_cast<uint64_t>(M) * N * e : 0;
-    l.args.rows = static_cast<uint32_t>(M);
+    l.args.rows = static_cast<uint32_t>(rows);
     l.args.tile_m = static_cast<uint32_t>(p.tile_m);
     l.args.tile_row_bytes = static_cast<uint32_t>(p.tile_n) * e;
     l.args.vecs_per_row_log2 = static_cast<uint32_t>(log2_exact(static_cast<uint64_t>(p.tile_n) * e / p.vec_bytes));

@@ -85,20 +85,52 @@ def test_plan_strided_group_uses_group_rank():
     assert p.rank_block_offset == 2 * 1024 * 4096 * 2
 
 
+# M = 63: the block's size is N*e*63, a multiple of 16 only when the row is; M = 64 would let the
+# kernels view the block as rows of a multiple of 16 bytes (test_plan_row_view)
 @pytest.mark.parametrize("N,dtype,inp,off,vec", [
     (4096, "f16", INPUT, 0, 16), (4100, "f16", INPUT, 0, 8), (4098, "f16", INPUT, 0, 4),
     (4097, "f16", INPUT, 0, 2), (4096, "f16", INPUT + 8, 0, 8), (4096, "f16", INPUT, 2, 2),
     (4096, "f32", INPUT, 4, 4), (4097, "f32", INPUT, 0, 4), (4098, "f32", INPUT, 0, 8),
 ])
 def test_plan_vector_width_follows_alignment(N, dtype, inp, off, vec):
-    p = plan(N=N, dtype=dtype, inp=inp, off=off, M=64)
+    p = plan(N=N, dtype=dtype, inp=inp, off=off, M=63)
     assert p.vec_bytes == vec
+
+
+# A dense block of M x N elements is M*N*e contiguous bytes.  When rows are not a multiple of 16 bytes
+# but the block is (and the input and output block are 16-byte aligned), the kernels walk it as rows of
+# cols elements, cols*e a multiple of 16: the divisor of the block's 16-byte vector count nearest N*e/16.
+@pytest.mark.parametrize("M,N,dtype,inp,off,vec,tiles", [
+    (1000, 4100, "f16", INPUT, 0, 16, (129, 16)),   # 512500 vectors: rows of 500 (4000 elements), 1025 rows
+    (64, 4100, "f16", INPUT, 0, 16, None),
+    (64, 4097, "f16", INPUT, 0, 16, None),
+    (64, 4098, "f32", INPUT, 0, 16, None),
+    (64, 4100, "f16", INPUT + 8, 0, 8, (8, 17)),     # input 8-byte aligned: rows as given
+    (64, 4100, "f16", INPUT, 8, 8, (8, 17)),         # output block 8-byte aligned
+    (1, 4100, "f16", INPUT, 0, 8, (1, 17)),          # one row: 8200 bytes, not a multiple of 16
+])
+def test_plan_row_view(M, N, dtype, inp, off, vec, tiles):
+    p = plan(N=N, dtype=dtype, inp=inp, off=off, M=M)
+    assert p.vec_bytes == vec
+    if tiles:
+        assert (p.tiles_m, p.tiles_n) == tiles
+    # the tiles cover the block's bytes exactly once however it is viewed
+    e = 4 if dtype == "f32" else 2
+    assert p.tiles_m * 8 >= M * N * e // (p.tiles_n * 256 * e) and p.bytes_read == M * N * e
+
+
+def test_plan_row_view_only_when_the_tile_fits():
+    # a 1x256 fp16 tile is 32 vectors of 16 bytes, fewer than 256 threads: the rows stay as given, 2-byte vectors
+    p = plan(M=64, N=4097, tm=1, tn=256)
+    assert p.vec_bytes == 2 and (p.tiles_m, p.tiles_n) == (64, 17)
+    p = plan_a2a(M=16, N=4095, tm=1, tn=256)
+    assert p.vec_bytes == 2 and (p.tiles_m, p.tiles_n) == (16, 16)
 
 
 def test_plan_programs_and_tiles():
     p = plan(M=64, N=256, progs=4)        # 8 tiles over 4 programs
     assert p.total_tiles == 8 and p.n_programs * (p.threads // 256) <= 8
-    p = plan(M=1000, N=4100)              # partial tiles in both directions
+    p = plan(M=1000, N=4100, inp=INPUT + 8)   # partial tiles in both directions (8-byte aligned input)
     assert p.tiles_m == 125 and p.tiles_n == 17
     p = plan(M=8, N=256, progs=10_000)    # more programs than tiles: only one launched
     assert p.n_programs == 1
@@ -247,7 +279,7 @@ def test_plan_destination_groups(W, group, applied):
     (dict(group=-1), ag.AG_ERR_INVALID_ARG),
     (dict(group=2, sched=1), ag.AG_ERR_INVALID_ARG),
     (dict(sched=2), ag.AG_ERR_INVALID_ARG),
-    (dict(group=2, M=64, N=4097, dtype="f32"), ag.AG_ERR_UNSUPPORTED),   # 4-byte vectors: no grouped kernel
+    (dict(group=2, M=63, N=4097, dtype="f32"), ag.AG_ERR_UNSUPPORTED),   # 4-byte vectors: no grouped kernel
 ])
 def test_plan_ex_rejects(kw, status):
     assert status_of(plan_ex, **kw)[0] == status
@@ -314,7 +346,7 @@ def test_plan_all_to_all_rejects(kw, status):
 
 @pytest.mark.parametrize("N,vec,vpt", [(4096, 16, 1), (4092, 8, 2), (4094, 4, 4), (4095, 2, 8)])
 def test_plan_all_to_all_default_tile_fits_every_vector_width(N, vec, vpt):
-    p = plan_a2a(M=16, N=N)
+    p = plan_a2a(M=15, N=N)   # 15 rows: the chunk is a multiple of 16 bytes only when its rows are
     assert (p.vec_bytes, p.vectors_per_thread) == (vec, vpt)
 
 
