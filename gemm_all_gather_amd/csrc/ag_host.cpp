@@ -174,12 +174,19 @@ ag_status_t check_group(const ag_heap_geometry_t* geom, int W, int rank_start, i
 }
 
 // Tuning constants of the copy kernel: concurrent 256-thread tile slices per
-// workgroup (1 measured best or equal at 64-256 programs).
+// workgroup.  One measured best at 128 and 256 programs; launches on fewer
+// than half the CUs take up to four (at 64 programs: 5.26 against 4.91 TB/s
+// at W=8, 1024x4096 fp16, 2.55 against 2.47-2.50 at 16384x8192; two slices
+// were 3% slower on the larger shape).
 #ifndef AG_COPY_MAX_SLICES
 #define AG_COPY_MAX_SLICES 1
 #endif
+#ifndef AG_COPY_NARROW_SLICES
+#define AG_COPY_NARROW_SLICES 4
+#endif
 constexpr int kCopyMaxVpt = 8;
 constexpr int kCopyMaxSlices = AG_COPY_MAX_SLICES;
+constexpr uint64_t kCopyNarrowSlices = AG_COPY_NARROW_SLICES;   // launches on fewer than half the CUs
 
 }  // namespace
 
@@ -510,7 +517,9 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
         grid = per_dest * W;
     } else {
         // concurrent tiles per program: up to kCopyMaxSlices while every slice still gets a tile
-        while (!a2a && slices < static_cast<uint64_t>(kCopyMaxSlices) && programs * slices * 2 <= total) slices *= 2;
+        const uint64_t max_slices = 2 * programs < static_cast<uint64_t>(geom->num_cus) ? kCopyNarrowSlices
+                                                                                     : static_cast<uint64_t>(kCopyMaxSlices);
+        while (!a2a && slices < max_slices && programs * slices * 2 <= total) slices *= 2;
         grid = std::min<uint64_t>(programs, ceil_div(total, slices));
     }
     if (grid >= (uint64_t{1} << 31)) return fail(AG_ERR_UNSUPPORTED, "n_programs too large");
