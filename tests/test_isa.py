@@ -299,7 +299,8 @@ def test_report_registers(asm, capsys):
                 rows.append((sym, _meta(asm[src], sym)))
     assert rows
     # the instantiations the benchmark workloads run, then a summary over all of them
-    bench = [r"ag_copy_kernelILi16ELi8ELi1ELi0ELb0E", r"ag_a2a_kernelILi16ELi8ELi1E",
+    bench = [r"ag_copy_kernelILi16ELi8ELi1ELi0ELb0ELb1E", r"ag_copy_kernelILi16ELi8ELi1ELi0ELb0ELb0E",
+             r"ag_a2a_kernelILi16ELi8ELi2ELb1E",
              r"ag_gemm_kernelILb0ELi8E\S*CfgILi256ELi224E\S*ELb0EEEv", r"ag_gemm_kernelILb1ELi8E\S*CfgILi256ELi224E\S*ELb0EEEv",
              r"ag_gemm_kernelILb0ELi8E\S*CfgILi128ELi128E\S*ELb0EEEv", r"ag_gemm_kernelILb0ELi1E\S*CfgILi256ELi224E\S*ELb0EEEv",
              r"ag_gemm_kernelILb0ELi8E\S*CfgILi256ELi224E\S*ELb1EEEv", r"ag_gemm_kernelILb0ELi8E\S*CfgILi128ELi128E\S*ELb1EEEv"]
