@@ -252,19 +252,22 @@ ag_status_t ag_heap_wrap(void* dev_slab, int n_ranks, size_t bytes_per_rank, ag_
         if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
         if ((attr.type != hipMemoryTypeDevice && !attr.isManaged) || attr.device != dev)
             return fail(AG_ERR_INVALID_ARG, "dev_slab is not device memory of the current device %d", dev);
+        // the allocation's extent, where the runtime knows it (memory mapped through the virtual
+        // memory API may not report one: then only the checks above apply)
         void* base = nullptr;
         size_t size = 0;
         e = hipMemGetAddressRange(reinterpret_cast<hipDeviceptr_t*>(&base), &size, dev_slab);
-        if (e != hipSuccess) {
+        if (e != hipSuccess || base == nullptr || size == 0) {
             (void)hipGetLastError();
-            return fail(AG_ERR_INVALID_ARG, "the allocation holding dev_slab is unknown (%s)", hipGetErrorString(e));
+        } else {
+            const uint64_t need = static_cast<uint64_t>(n_ranks) * bytes_per_rank;
+            const uint64_t avail = reinterpret_cast<uint64_t>(base) + size - reinterpret_cast<uint64_t>(dev_slab);
+            if (need > avail)
+                return fail(AG_ERR_INVALID_ARG,
+                            "%d regions of %zu bytes need %llu bytes, the allocation holds %llu from dev_slab", n_ranks,
+                            bytes_per_rank, static_cast<unsigned long long>(need),
+                            static_cast<unsigned long long>(avail));
         }
-        const uint64_t need = static_cast<uint64_t>(n_ranks) * bytes_per_rank;
-        const uint64_t avail = reinterpret_cast<uint64_t>(base) + size - reinterpret_cast<uint64_t>(dev_slab);
-        if (need > avail)
-            return fail(AG_ERR_INVALID_ARG, "%d regions of %zu bytes need %llu bytes, the allocation holds %llu from dev_slab",
-                        n_ranks, bytes_per_rank, static_cast<unsigned long long>(need),
-                        static_cast<unsigned long long>(avail));
     }
     auto core = std::make_shared<HeapCore>();
     core->slab = dev_slab;

@@ -132,7 +132,8 @@ ag_status_t ag_heap_create(int n_ranks, size_t bytes_per_rank, ag_heap_t** out);
  * bytes_per_rank a non-zero multiple of 256.  dev_slab must be device (or
  * managed) memory of the current device, and its allocation must hold the
  * n_ranks*bytes_per_rank bytes from dev_slab on (AG_ERR_INVALID_ARG
- * otherwise: checked with hipPointerGetAttributes and hipMemGetAddressRange).
+ * otherwise: checked with hipPointerGetAttributes and, where the runtime
+ * reports the allocation's extent, hipMemGetAddressRange).
  * The library allocates and owns only the base table; the caller keeps the
  * slab alive until every handle on it is destroyed. */
 ag_status_t ag_heap_wrap(void* dev_slab, int n_ranks, size_t bytes_per_rank, ag_heap_t** out);

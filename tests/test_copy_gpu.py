@@ -236,6 +236,44 @@ def test_wrap_rejects_host_memory_and_short_slabs():
         th.close()
 
 
+_EXPANDABLE = r"""
+import os, sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np, torch
+from gemm_all_gather_amd import binding as ag
+from gemm_all_gather_amd import inputs as gen
+from oracle import all_gather_oracle
+R, W, M, N, S = 4, 4, 40, 264, 1 << 20
+slab = torch.zeros(R * S, dtype=torch.uint8, device="cuda")
+heap = ag.Heap.wrap(slab, R, S)
+ins = [gen.uniform_pm1((M, N), "f16", 31, j) for j in range(W)]
+dev = [torch.from_numpy(x.view(np.uint8).reshape(-1).copy()).cuda() for x in ins]
+before = slab.cpu().numpy()
+views = [heap.view(j) for j in range(W)]
+for j in range(W):
+    ag.all_gather(views[j], W, 0, 1, dev[j], 0, M, N, "f16")
+torch.cuda.synchronize()
+assert np.array_equal(slab.cpu().numpy(), all_gather_oracle(before, S, ins, 0, 1, 0))
+print("expandable-segments slab: bit-exact")
+"""
+
+
+def test_wrap_accepts_expandable_segment_memory():
+    """A slab from PyTorch's expandable-segments allocator (memory mapped through the virtual memory API)
+    is accepted and gathered bit-exactly (a separate process: the allocator is chosen at start-up)."""
+    require_gpu()
+    import os
+    import subprocess
+    import sys
+    log("ag_heap_wrap over an expandable-segments allocation (subprocess)")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, PYTORCH_HIP_ALLOC_CONF="expandable_segments:True",
+               PYTORCH_CUDA_ALLOC_CONF="expandable_segments:True")
+    r = subprocess.run([sys.executable, "-c", _EXPANDABLE, root], env=env, capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert "bit-exact" in r.stdout
+
+
 def test_launching_entry_point_rejects_invalid_arguments():
     require_gpu()
     log("ag_all_gather validation on the launching entry point")
