@@ -163,6 +163,15 @@ def test_all_to_all_tiny_sweep(W, start, stride, M, N):
     _a2a(8, _size(W, M, N, e, off), W, start, stride, M, N, dtype, off, tile, programs, seed=W + M + N)
 
 
+def test_all_to_all_row_view():
+    # chunks of 1000 x 4100 fp16: rows of 8200 bytes, chunks of 512,500 16-byte vectors, so the kernel walks
+    # them as rows of 4000 elements with 16-byte vectors
+    p = ag.plan_all_to_all(ag.Geometry(slab_addr=1 << 32, bytes_per_rank=_size(4, 1000, 4100, 2, 0), n_ranks=8,
+                                       rank=1, num_cus=256), 4, 1, 2, 1 << 44, 0, 1000, 4100, "f16", 8, 256, 64)
+    assert p.vec_bytes == 16 and (p.tiles_m, p.tiles_n) == (129, 16)
+    _a2a(8, _size(4, 1000, 4100, 2, 0), 4, 1, 2, 1000, 4100, "f16", 0, (8, 256), 64, seed=13)
+
+
 def test_all_to_all_edges_and_streams():
     _a2a(8, _size(4, 125, 4100, 2, 64), 4, 1, 2, 125, 4100, "f16", 64, (8, 256), 64, seed=11, streams=True)
     _a2a(8, _size(8, 13, 520, 4, 0), 8, 0, 1, 13, 520, "f32", 0, (8, 256), 5, seed=12)
