@@ -1,19 +1,23 @@
 """Benchmark of the hot path on one MI355X: multi-destination all-gather + fused GEMM + all-gather.
 
-One step = one complete logical all-gather job on one GPU:
+One step = one complete logical all-gather job and one fused job on one GPU:
   * all-gather: every one of the W=8 logical ranks calls ag_all_gather on its
-    1024 x 4096 fp16 input (tile 8x256, 128 programs), so every heap region
-    ends up with the 8192 x 4096 gathered tensor;
+    16384 x 8192 fp16 input (uniform[-1,1), tile 8x256, 256 programs), so every
+    heap region ends up with the 131072 x 8192 gathered tensor (2.4 GB of HBM
+    traffic per call, far beyond the last-level cache);
   * fused: every one of the 8 logical ranks calls ag_gemm_all_gather with
-    A_g 16384 x 8192 and the shared B 8192 x 3584 (fp16, fp32 accumulate),
-    so every region ends up with the 131072 x 3584 gathered C (the fused
-    workload whose MFMA-utilisation target is stated; --fused-m 1024 selects
-    the M_local = 1024 variant).
+    A_g 16384 x 8192 and the shared B 8192 x 3584 (fp16 ~ N(0,1)/sqrt(K), fp32
+    accumulate), so every region ends up with the 131072 x 3584 gathered C
+    (--fused-m 1024 selects the M_local = 1024 variant).
 Inputs are seeded synthetic tensors already resident in HBM.
 
 Printed: one JSON line.  value = all-gather HBM GB/s over the whole job
 ((1+W)*M_local*N*e bytes per call, W calls per step); the fused path's
-TFLOP/s is reported in the "fused" object, each with its roofline.
+TFLOP/s is reported in the "fused" object, each with its roofline.  The
+"context" object holds the other program counts and element types of the
+16384 x 8192 all-gather, the 1024 x 4096 all-gather (75 MB per call, partly
+held by the last-level cache), the variants, the all-to-all, edge shapes,
+the other fused workloads and a plain copy/fill calibration.
 """
 
 from __future__ import annotations
@@ -34,9 +38,11 @@ METRIC = "all-gather achieved HBM GB/s (+% peak); fused GEMM+AG TFLOP/s (+% MFMA
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 
-# all-gather workload: W=8 logical ranks, 1024 x 4096 fp16 per rank, tile 8x256; of the program
-# counts the workload is defined for (64/128/256, all three timed in "context"), 128
-AG_W, AG_M, AG_N, AG_DTYPE, AG_TILE, AG_PROGRAMS = 8, 1024, 4096, "f16", (8, 256), 128
+# all-gather workload: W=8 logical ranks, 16384 x 8192 fp16 per rank, tile 8x256, 256 programs (the CU
+# count; 64 and 128, and bf16 and fp32, are timed in "context")
+AG_W, AG_M, AG_N, AG_DTYPE, AG_TILE, AG_PROGRAMS = 8, 16384, 8192, "f16", (8, 256), 256
+# the smaller all-gather workload (context): 1024 x 4096 fp16 per rank, 75 MB per call
+SM_M, SM_N, SM_PROGRAMS = 1024, 4096, 128
 # fused workload: W=8, M_local 16384, K 8192, N 3584, fp16
 FU_W, FU_N, FU_K, FU_DTYPE = 8, 3584, 8192, "f16"
 FU_M = 16384
@@ -64,29 +70,57 @@ def _traffic(summary: str, source: str, per_launch_alg: float):
     return float(m_bytes.group(1))
 
 
-def _cpu_baseline_copy(seconds: float):
-    """The oracle's all-gather of the same workload on the host cores (a bounded sample)."""
+def _host_threads() -> int:
+    """Host threads for the CPU baseline: the process's cores, at most the OpenMP thread count set for it."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", cores))
+    except ValueError:
+        cap = cores
+    return max(1, min(cores, cap))
+
+
+def _cpu_baseline_copy(seconds: float, host_input):
+    """The oracle's store of one rank's input into the W member regions, on the host cores (bounded sample).
+
+    One call's work: the 16384 x 8192 fp16 input (the same bytes as rank 0's device input) written at the
+    rank's row block of W preallocated host regions (each sized for the gathered output), with the oracle's
+    multi-destination store (oracle.store_to_members); the rows are split among the threads, each thread
+    storing its rows to all W regions.
+    """
     import numpy as np
-    from gemm_all_gather_amd import inputs as gen
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
 
-    e = 2
-    blk = AG_M * AG_N * e
-    S = AG_W * blk
-    ins = [gen.uniform_pm1((AG_M, AG_N), AG_DTYPE, 1, j) for j in range(AG_W)]
-    slab = np.zeros(AG_W * S, dtype=np.uint8)
-    oracle.all_gather_oracle(slab, S, ins, 0, 1, 0)        # warm-up
+    threads = _host_threads()
+    data = np.ascontiguousarray(host_input).view(np.uint8).reshape(-1)
+    blk = data.size
+    regions = [np.empty(AG_W * blk, dtype=np.uint8) for _ in range(AG_W)]
+    g = 0                                              # the calling rank's group index
+    bounds = [blk * t // threads // 4096 * 4096 for t in range(threads)] + [blk]
+    pool = ThreadPoolExecutor(max_workers=threads)
+
+    def call():
+        futs = [pool.submit(oracle.store_to_members, regions, g * blk + bounds[t], data[bounds[t]:bounds[t + 1]])
+                for t in range(threads)]
+        for f in futs:
+            f.result()
+
+    call()                                             # warm-up: first touch of the regions
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.all_gather_oracle(slab, S, ins, 0, 1, 0)
+        call()
         reps += 1
         if time.perf_counter() - t0 >= seconds:
             break
     dt = (time.perf_counter() - t0) / reps
-    job_bytes = AG_W * (1 + AG_W) * blk
-    return {"value": job_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} whole all-gather jobs (W=8, {AG_M}x{AG_N} fp16 per rank, full 8-region heap "
-                      f"copy included) in {reps * dt:.1f} s with numpy on 1 host thread"}
+    pool.shutdown()
+    del regions
+    call_bytes = (1 + AG_W) * blk
+    return {"value": call_bytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} calls of one rank's all-gather (W={AG_W}, its {AG_M}x{AG_N} fp16 input stored at its "
+                      f"row block of {AG_W} preallocated host regions by oracle.store_to_members, rows split over "
+                      f"{threads} threads) in {reps * dt:.1f} s; GB/s = (1+W)*M_local*N*e per call"}
 
 
 def _cpu_baseline_fused(seconds: float):
@@ -95,144 +129,194 @@ def _cpu_baseline_fused(seconds: float):
     from gemm_all_gather_amd import inputs as gen
     import oracle
 
-    threads = len(os.sched_getaffinity(0))
+    threads = _host_threads()
     rows = 64
     a = gen.normal_scaled((rows, FU_K), FU_DTYPE, FU_K ** -0.5, 2, 0)
     b = gen.normal_scaled((FU_N, FU_K), FU_DTYPE, FU_K ** -0.5, 3)
-    oracle.gemm_oracle(a[:8], b, FU_DTYPE, "nk")             # warm-up
+    regions = [np.empty(rows * FU_N * 2, dtype=np.uint8) for _ in range(FU_W)]
+
+    def call():
+        c = oracle.gemm_oracle(a, b, FU_DTYPE, "nk")
+        oracle.store_to_members(regions, 0, c.view(np.uint8).reshape(-1))
+
+    call()                                             # warm-up
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.gemm_oracle(a, b, FU_DTYPE, "nk")
+        call()
         reps += 1
         if time.perf_counter() - t0 >= seconds:
             break
     dt = (time.perf_counter() - t0) / reps
     flops = 2.0 * rows * FU_N * FU_K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} x {rows} output rows of one rank's {FU_M}x{FU_N}x{FU_K} fp16 product "
-                      f"(float64 numpy matmul + rounding), {reps * dt:.1f} s; BLAS may use up to {threads} threads"}
+            "sample": f"{reps} x {rows} output rows of one rank's {FU_M}x{FU_N}x{FU_K} fp16 product (float64 numpy "
+                      f"matmul, rounding, stores to {FU_W} host regions), {reps * dt:.1f} s; BLAS threads up to "
+                      f"{threads}"}
 
 
-def _context(args, stream, timed, views, ins, geom):
-    """Context measurements beside the headline (each job = the 8 ranks' calls, timed like it).
+def _device_uniform(n_elems: int, dtype: str, seed: int):
+    """Seeded uniform[-1,1) values drawn on the device (float32 2u - 1, rounded to the storage type), as bytes."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    x = torch.rand(n_elems, generator=g, dtype=torch.float32, device="cuda") * 2.0 - 1.0
+    return x.to(tdt).view(torch.uint8)
 
-    * the all-gather workload at the three program counts it is defined for;
-    * destination groups 1/2/4 and the partitioned schedule (all-gather variants);
-    * the all-to-all on the same heap: W=8, 8 chunks of 1024x4096 fp16 per rank, tile and partitioned
-      schedules;
-    * the all-gather at 16384x8192 per rank in fp16, bf16 and fp32 (2.4 / 2.4 / 4.8 GB per call);
-    * the edge shapes: 1000x4100 fp16 (8-byte vectors, partial last column tile) at W=8, and the
-      strided group of ranks 1, 3, 5, 7 (W=4) at 1000x4100 and 16384x8192.
+
+def _device_normal(n_elems: int, dtype: str, scale: float, seed: int):
+    """Seeded N(0,1)*scale values drawn on the device in float32, rounded to the storage type, as bytes."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    x = torch.randn(n_elems, generator=g, dtype=torch.float32, device="cuda") * scale
+    return x.to(tdt).view(torch.uint8)
+
+
+class _Workload:
+    """An 8-region heap sized for one all-gather shape, with every member's device input."""
+
+    def __init__(self, M, N, dtype, W=AG_W, start=0, stride=1, seed=1, n_regions=8, out_bytes=None):
+        import torch
+        from gemm_all_gather_amd import binding as ag
+        self.M, self.N, self.dtype, self.W, self.start, self.stride = M, N, dtype, W, start, stride
+        self.e = 4 if dtype == "f32" else 2
+        self.blk = M * N * self.e
+        # every region sized for the gathered output (2 MiB multiples)
+        out_bytes = W * self.blk if out_bytes is None else out_bytes
+        self.S = -(-out_bytes // (2 << 20)) * (2 << 20)
+        self.slab = torch.empty(n_regions * self.S, dtype=torch.uint8, device="cuda")
+        self.slab.zero_()
+        self.heap = ag.Heap.wrap(self.slab, n_regions, self.S)
+        self.members = [start + i * stride for i in range(W)]
+        self.views = {r: self.heap.view(r) for r in self.members}
+        self.ins = [_device_uniform(M * N, dtype, seed * 100 + i) for i in range(W)]
+        self.geom = self.views[start].geometry()
+
+    def job(self, ag, stream, tile=(0, 0), programs=0, dest_group=0, schedule="tiles"):
+        """All W members' calls, in group order."""
+        def run():
+            for i, r in enumerate(self.members):
+                if dest_group == 0 and schedule == "tiles":
+                    ag.all_gather(self.views[r], self.W, self.start, self.stride, self.ins[i], 0, self.M, self.N,
+                                  self.dtype, tile[0], tile[1], programs, stream)
+                else:
+                    ag.all_gather_ex(self.views[r], self.W, self.start, self.stride, self.ins[i], 0, self.M, self.N,
+                                     self.dtype, tile[0], tile[1], programs, dest_group, schedule, stream)
+        return run
+
+    def plan(self, ag, tile=(0, 0), programs=0):
+        return ag.plan_all_gather(self.geom, self.W, self.start, self.stride, self.ins[0], 0, self.M, self.N,
+                                  self.dtype, tile[0], tile[1], programs)
+
+    def close(self):
+        import torch
+        torch.cuda.synchronize()
+        for v in self.views.values():
+            v.destroy()
+        self.heap.destroy()
+        del self.slab, self.ins
+        torch.cuda.empty_cache()
+
+
+def _context(args, stream, timed, head):
+    """Context measurements beside the headline (each job = the group members' calls, timed like it).
+
+    * the 16384x8192 all-gather at 64/128/256 programs in fp16, bf16 and fp32;
+    * its variants: destination groups 1/2/4 and the partitioned schedule at 64/128/256 programs;
+    * the 1024x4096 all-gather at 64/128/256 programs (75 MB per call: partly held by the last-level
+      cache, so its rate exceeds what HBM sustains for the larger shape);
+    * the all-to-all: W=8, 8 chunks of 1024x4096 fp16 per rank, tile and partitioned schedules;
+    * the edge shapes: 1000x4100 fp16 (partial last column tile) at W=8, and the strided group of ranks
+      1, 3, 5, 7 (W=4) at 1000x4100 and 16384x8192.
     """
     import torch
     from gemm_all_gather_amd import binding as ag
 
-    steps = max(10, args.steps // 4)
     sub = argparse.Namespace(**vars(args))
-    sub.steps, sub.warmup = steps, max(2, args.warmup // 2)
-    blk = AG_M * AG_N * 2
-    per_call = (1 + AG_W) * blk
+    sub.steps, sub.warmup = max(20, args.steps // 5), max(10, args.warmup // 5)
+    ctx = {"steps": sub.steps, "warmup": sub.warmup}
 
-    def gbs(ms, bytes_per_call):
-        return round(AG_W * bytes_per_call / (ms / 1e3) / 1e9, 1)
+    def rate(wl, **kw):
+        ms, _ = timed(wl.job(ag, stream, **kw), sub)
+        return round(wl.W * (1 + wl.W) * wl.blk / (ms / 1e3) / 1e9, 1), ms
 
-    ctx = {"steps": steps}
-    res = {}
+    # the 16384 x 8192 all-gather: three program counts, three element types (fp16 is the headline heap)
+    big = {}
+    for dt in ("f16", "bf16", "f32"):
+        wl = head if dt == "f16" else _Workload(AG_M, AG_N, dt, seed=6)
+        big[dt] = {}
+        for P in (64, 128, 256):
+            gb, ms = rate(wl, tile=AG_TILE, programs=P)
+            p = wl.plan(ag, AG_TILE, P)
+            big[dt][str(P)] = {"GBs": gb, "frac": round(gb / HBM_PEAK_GBS, 4), "us_per_call": round(ms * 1e3 / wl.W, 2),
+                               "threads": p.threads, "vectors_per_thread": p.vectors_per_thread}
+        if wl is not head:
+            wl.close()
+    ctx["all_gather_16384x8192"] = big
+    # its variants on the headline heap: destination groups at 256 programs, the partitioned schedule
+    # (every destination reads the tile itself: 2*W*M*N*e HBM bytes per call)
+    ctx["all_gather_16384x8192_f16_by_dest_group"] = {str(G): rate(head, tile=AG_TILE, programs=AG_PROGRAMS,
+                                                                   dest_group=G)[0] for G in (1, 2, 4)}
+    part = {}
     for P in (64, 128, 256):
-        ms, _ = timed_sub(sub, timed, lambda P=P: [ag.all_gather(views[j], AG_W, 0, 1, ins[j], 0, AG_M, AG_N, AG_DTYPE,
-                                                                  *AG_TILE, P, stream) for j in range(AG_W)])
-        res[str(P)] = gbs(ms, per_call)
-    ctx["all_gather_GBs_by_programs"] = res
-    res = {}
-    for G in (1, 2, 4):
-        ms, _ = timed_sub(sub, timed, lambda G=G: [ag.all_gather_ex(views[j], AG_W, 0, 1, ins[j], 0, AG_M, AG_N,
-                                                                     AG_DTYPE, *AG_TILE, AG_PROGRAMS, G, 0, stream)
-                                                   for j in range(AG_W)])
-        res[str(G)] = gbs(ms, per_call)
-    ctx["all_gather_GBs_by_dest_group"] = res
-    res = {}
-    for P in (64, 128, 256):
-        ms, _ = timed_sub(sub, timed, lambda P=P: [ag.all_gather_ex(views[j], AG_W, 0, 1, ins[j], 0, AG_M, AG_N,
-                                                                     AG_DTYPE, *AG_TILE, P, 0, "partitioned", stream)
-                                                   for j in range(AG_W)])
-        # HBM bytes of the schedule: every destination reads the tile itself
-        res[str(P)] = gbs(ms, 2 * AG_W * blk)
-    ctx["partitioned_GBs_by_programs"] = res
+        ms, _ = timed(head.job(ag, stream, tile=AG_TILE, programs=P, schedule="partitioned"), sub)
+        part[str(P)] = round(head.W * 2 * head.W * head.blk / (ms / 1e3) / 1e9, 1)
+    ctx["all_gather_16384x8192_f16_partitioned_GBs_by_programs"] = part
+
+    # the 1024 x 4096 all-gather (75 MB per call)
+    small = _Workload(SM_M, SM_N, "f16", seed=2)
+    sm = {str(P): rate(small, tile=AG_TILE, programs=P)[0] for P in (64, 128, 256)}
+    ctx["all_gather_1024x4096_f16_cache_assisted_GBs_by_programs"] = sm
+    small.close()
 
     # all-to-all: each rank sends 8 chunks of 1024x4096 fp16 (64 MiB per rank); 8x512 tiles, two 16-byte
     # vectors per thread (measured 5.3 TB/s against 5.0 for 8x256 at 256 programs)
     A2A_TILE = (8, 512)
-    mc = AG_M
-    g = torch.Generator(device="cuda")
-    g.manual_seed(5)
-    a2a_in = [torch.randint(-32768, 32767, (AG_W * mc * AG_N,), generator=g, dtype=torch.int16, device="cuda")
-              for _ in range(AG_W)]
-    a2a_plan = ag.plan_all_to_all(geom, AG_W, 0, 1, a2a_in[0], 0, mc, AG_N, AG_DTYPE, *A2A_TILE, 256)
-    ms, _ = timed_sub(sub, timed, lambda: [ag.all_to_all(views[j], AG_W, 0, 1, a2a_in[j], 0, mc, AG_N, AG_DTYPE,
-                                                         *A2A_TILE, 256, stream) for j in range(AG_W)])
+    mc, n = SM_M, SM_N
+    # inputs of W chunks; regions sized for the exchanged output (W chunks of M_chunk x N)
+    a2a = _Workload(AG_W * mc, n, "f16", seed=5, out_bytes=AG_W * mc * n * 2)
+    a2a_in = a2a.ins
+    a2a_plan = ag.plan_all_to_all(a2a.geom, AG_W, 0, 1, a2a_in[0], 0, mc, n, "f16", *A2A_TILE, 256)
+    views = a2a.views
+    ms, _ = timed(lambda: [ag.all_to_all(views[j], AG_W, 0, 1, a2a_in[j], 0, mc, n, "f16", *A2A_TILE, 256, stream)
+                           for j in range(AG_W)], sub)
     a2a_bytes = a2a_plan.bytes_read + a2a_plan.bytes_written
     launch_s = ms / 1e3 / AG_W
     ctx["all_to_all"] = {
-        "workload": f"all-to-all W={AG_W}, {AG_W} chunks of {mc}x{AG_N} fp16 per rank, tile {A2A_TILE[0]}x{A2A_TILE[1]}, "
+        "workload": f"all-to-all W={AG_W}, {AG_W} chunks of {mc}x{n} fp16 per rank, tile {A2A_TILE[0]}x{A2A_TILE[1]}, "
                     f"{a2a_plan.n_programs} programs (8 calls per job)",
         "value": round(AG_W * a2a_bytes / (ms / 1e3) / 1e9, 1), "unit": "GB/s",
         "roofline": {"bound": "hbm", "achieved": round(a2a_bytes / launch_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(a2a_bytes / launch_s / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": _traffic(f"ag_a2a_kernel_w{AG_W}_{mc}x{AG_N}_f16_pmc.md", "ag_copy.hip", a2a_bytes),
+                     "traffic": _traffic(f"ag_a2a_kernel_w{AG_W}_{mc}x{n}_f16_pmc.md", "ag_copy.hip", a2a_bytes),
                      "alg_bytes_per_launch": a2a_bytes, "avg_launch_us": round(launch_s * 1e6, 3)},
     }
     # the partitioned schedule of the same exchange (program p copies one chunk to destination p mod W)
-    ms, _ = timed_sub(sub, timed, lambda: [ag.all_to_all_ex(views[j], AG_W, 0, 1, a2a_in[j], 0, mc, AG_N, AG_DTYPE,
-                                                            16, 512, 256, schedule="partitioned", stream=stream)
-                                           for j in range(AG_W)])
+    ms, _ = timed(lambda: [ag.all_to_all_ex(views[j], AG_W, 0, 1, a2a_in[j], 0, mc, n, "f16", 16, 512, 256,
+                                            schedule="partitioned", stream=stream) for j in range(AG_W)], sub)
     ctx["all_to_all"]["partitioned_16x512_256_programs_GBs"] = round(AG_W * a2a_bytes / (ms / 1e3) / 1e9, 1)
-    del a2a_in
+    a2a.close()
 
-    sub3 = argparse.Namespace(**vars(sub))
-    sub3.steps, sub3.warmup = 5, 1
-
-    def gather_rate(M3, N3, dtype, W3, start, stride, programs, seed):
-        """GB/s of one group's all-gather job ((1+W)*M*N*e per call) on a fresh 8-region heap."""
-        e3 = 4 if dtype == "f32" else 2
-        blk3 = M3 * N3 * e3
-        S3 = ((8 * blk3) // (2 << 20) + 1) * (2 << 20)
-        slab3 = torch.empty(8 * S3, dtype=torch.uint8, device="cuda")
-        heap3 = ag.Heap.wrap(slab3, 8, S3)
-        views3 = [heap3.view(r) for r in range(8)]
-        members = [start + i * stride for i in range(W3)]
-        g.manual_seed(seed)
-        in3 = [torch.randint(-32768, 32767, (blk3 // 2,), generator=g, dtype=torch.int16, device="cuda")
-               for _ in members]
-        ms, _ = timed_sub(sub3, timed, lambda: [ag.all_gather(views3[r], W3, start, stride, in3[i], 0, M3, N3,
-                                                              dtype, 0, 0, programs, stream)
-                                                for i, r in enumerate(members)])
-        for v in views3:
-            v.destroy()
-        heap3.destroy()
-        del slab3, in3
-        torch.cuda.empty_cache()
-        return round(W3 * (1 + W3) * blk3 / (ms / 1e3) / 1e9, 1)
-
-    # the all-gather at 16384 x 8192 per rank (2.4 GB per call in 16 bits), three element types
-    ctx["all_gather_16384x8192_256_programs_GBs_by_dtype"] = {
-        dt: gather_rate(16384, 8192, dt, AG_W, 0, 1, 256, 6) for dt in ("f16", "bf16", "f32")}
-    # the edge shapes: rows of 4100 elements (8-byte vectors, partial last column tile); the strided
-    # group of ranks 1, 3, 5, 7 (W=4) at both sizes
-    ctx["all_gather_edges_GBs"] = {
-        "1000x4100_f16_W8": gather_rate(1000, 4100, "f16", AG_W, 0, 1, 256, 7),
-        "1000x4100_f16_W4_group_1_2": gather_rate(1000, 4100, "f16", 4, 1, 2, 256, 8),
-        "16384x8192_f16_W4_group_1_2": gather_rate(16384, 8192, "f16", 4, 1, 2, 256, 9),
-    }
+    # the edge shapes: rows of 4100 elements (partial last column tile); the strided group of ranks
+    # 1, 3, 5, 7 (W=4) at both sizes
+    edges = {}
+    for name, M, N, W, start, stride, seed in (("1000x4100_f16_W8", 1000, 4100, AG_W, 0, 1, 7),
+                                               ("1000x4100_f16_W4_group_1_2", 1000, 4100, 4, 1, 2, 8),
+                                               ("16384x8192_f16_W4_group_1_2", 16384, 8192, 4, 1, 2, 9)):
+        wl = _Workload(M, N, "f16", W=W, start=start, stride=stride, seed=seed)
+        edges[name] = rate(wl, programs=256)[0]
+        wl.close()
+    ctx["all_gather_edges_GBs"] = edges
     return ctx
 
 
 def _context_fused(args, stream, timed, views, fu_off):
     """The fused workload at M_local 1024 (fp16), at M_local 16384 in bf16, and at M_local 16384 in fp16 with B
     stored N-contiguous (a row-major K x N matrix), W=8, timed like the headline."""
-    import numpy as np
     import torch
     from gemm_all_gather_amd import binding as ag
-    from gemm_all_gather_amd import inputs as gen
 
     res = {}
     region = views[0].geometry().bytes_per_rank
@@ -257,19 +341,16 @@ def _context_fused(args, stream, timed, views, fu_off):
             vws, off = views, fu_off
         if off + FU_W * M * FU_N * 2 > (region if own is None else S):
             continue
-        fa = [torch.from_numpy(gen.normal_scaled((M, FU_K), dtype, FU_K ** -0.5, 12, j).view(np.uint8)
-                               .reshape(-1).copy()).cuda() for j in range(FU_W)]
-        b_nk = gen.normal_scaled((FU_N, FU_K), dtype, FU_K ** -0.5, 13)
-        b_host = b_nk if layout == "k" else np.ascontiguousarray(b_nk.T)
+        fa = [_device_normal(M * FU_K, dtype, FU_K ** -0.5, 1200 + j) for j in range(FU_W)]
+        fb = _device_normal(FU_N * FU_K, dtype, FU_K ** -0.5, 1300)    # the N x K (or K x N) B: same count
         ldb = FU_K if layout == "k" else FU_N
-        fb = torch.from_numpy(b_host.view(np.uint8).reshape(-1).copy()).cuda()
         ms, _ = timed(lambda: [ag.gemm_all_gather_ex(vws[j], FU_W, 0, 1, fa[j], FU_K, fb, ldb, off, M, FU_N,
                                                      FU_K, dtype, 0, 0, 0, 0, b_layout=layout, stream=stream)
                                for j in range(FU_W)], sub)
         flops = 2.0 * M * FU_N * FU_K
         tf = FU_W * flops / (ms / 1e3) / 1e12
         res[name] = {"TFLOPs": round(tf, 1), "frac_of_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                     "us_per_call": round(ms * 1e3 / FU_W, 1)}
+                     "us_per_call": round(ms * 1e3 / FU_W, 1), "warmup": sub.warmup, "steps": sub.steps}
         del fa, fb
         if own is not None:
             torch.cuda.synchronize()
@@ -307,10 +388,6 @@ def _calibration(stream):
     return out
 
 
-def timed_sub(sub, timed, job):
-    return timed(job, sub)
-
-
 def main() -> int:
     global FU_M
     ap = argparse.ArgumentParser()
@@ -323,9 +400,9 @@ def main() -> int:
     ap.add_argument("--only", choices=["all", "copy", "fused"], default="all",
                     help="restrict the timed step to one kernel (profiling runs)")
     ap.add_argument("--no-context", action="store_true",
-                    help="skip the context measurements (program counts, destination groups, partitioned "
-                         "schedule, all-to-all, 16384x8192 all-gather in three types, edge shapes, the fused "
-                         "workload at M_local 1024 and in bf16, plain copy/fill calibration)")
+                    help="skip the context measurements (program counts and element types, variants, the "
+                         "1024x4096 all-gather, all-to-all, edge shapes, the other fused workloads, plain "
+                         "copy/fill calibration)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB "
                          "(reference for HBM byte counters)")
@@ -336,60 +413,39 @@ def main() -> int:
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
     from gemm_all_gather_amd import binding as ag
-    from gemm_all_gather_amd import inputs as gen
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ag.lib()
     dev_props = torch.cuda.get_device_properties(0)
     stream = torch.cuda.current_stream()
 
-    # ---------------- all-gather setup
-    e = 2
-    blk = AG_M * AG_N * e
-    # each workload has a heap of its own, every region sized for its gathered output (2 MiB multiples)
-    S = -(-(AG_W * blk) // (2 << 20)) * (2 << 20)
-    slab = torch.empty(AG_W * S, dtype=torch.uint8, device="cuda")
-    slab.zero_()
-    heap = ag.Heap.wrap(slab, AG_W, S)
-    views = [heap.view(r) for r in range(AG_W)]
-    ins = [torch.from_numpy(gen.uniform_pm1((AG_M, AG_N), AG_DTYPE, 1, j).view(np.uint8).reshape(-1).copy()).cuda()
-           for j in range(AG_W)]
-    geom = views[0].geometry()
-    ag_plan = ag.plan_all_gather(geom, AG_W, 0, 1, ins[0], 0, AG_M, AG_N, AG_DTYPE, *AG_TILE, AG_PROGRAMS)
-
-    def copy_job():
-        if args.only == "fused":
-            return
-        for j in range(AG_W):
-            ag.all_gather(views[j], AG_W, 0, 1, ins[j], 0, AG_M, AG_N, AG_DTYPE, AG_TILE[0], AG_TILE[1],
-                          AG_PROGRAMS, stream)
+    # ---------------- all-gather setup: 16384 x 8192 fp16 per rank, 8 regions of 2 GiB
+    head = _Workload(AG_M, AG_N, AG_DTYPE, seed=1) if args.only != "fused" else None
+    ag_plan = head.plan(ag, AG_TILE, AG_PROGRAMS) if head is not None else None
+    copy_job = head.job(ag, stream, tile=AG_TILE, programs=AG_PROGRAMS) if head is not None else None
 
     # ---------------- fused setup
     fused_ok = args.only != "copy"
-    fa = [torch.from_numpy(gen.normal_scaled((FU_M, FU_K), FU_DTYPE, FU_K ** -0.5, 2, j).view(np.uint8)
-                           .reshape(-1).copy()).cuda() for j in range(FU_W)]
-    fb = torch.from_numpy(gen.normal_scaled((FU_N, FU_K), FU_DTYPE, FU_K ** -0.5, 3).view(np.uint8)
-                          .reshape(-1).copy()).cuda()
-    fblk = FU_M * FU_N * 2
-    SF = -(-(FU_W * fblk) // (2 << 20)) * (2 << 20)
-    fslab = torch.empty(FU_W * SF, dtype=torch.uint8, device="cuda")
-    fslab.zero_()
-    fheap = ag.Heap.wrap(fslab, FU_W, SF)
-    fviews = [fheap.view(r) for r in range(FU_W)]
-    fu_off = 0
+    if fused_ok:
+        fa = [_device_normal(FU_M * FU_K, FU_DTYPE, FU_K ** -0.5, 200 + j) for j in range(FU_W)]
+        fb = _device_normal(FU_N * FU_K, FU_DTYPE, FU_K ** -0.5, 300)
+        fblk = FU_M * FU_N * 2
+        SF = -(-(FU_W * fblk) // (2 << 20)) * (2 << 20)
+        fslab = torch.empty(FU_W * SF, dtype=torch.uint8, device="cuda")
+        fslab.zero_()
+        fheap = ag.Heap.wrap(fslab, FU_W, SF)
+        fviews = [fheap.view(r) for r in range(FU_W)]
+        fu_off = 0
 
-    def fused_job():
-        if args.only == "copy":
-            return
-        for j in range(FU_W):
-            ag.gemm_all_gather(fviews[j], FU_W, 0, 1, fa[j], FU_K, fb, FU_K, fu_off, FU_M, FU_N, FU_K, FU_DTYPE,
-                               0, 0, 0, 0, stream)
+        def fused_job():
+            for j in range(FU_W):
+                ag.gemm_all_gather(fviews[j], FU_W, 0, 1, fa[j], FU_K, fb, FU_K, fu_off, FU_M, FU_N, FU_K, FU_DTYPE,
+                                   0, 0, 0, 0, stream)
 
-    fu_plan = ag.plan_gemm_all_gather(fviews[0].geometry(), FU_W, 0, 1, fa[0], FU_K, fb, FU_K, fu_off, FU_M, FU_N,
-                                      FU_K, FU_DTYPE)
+        fu_plan = ag.plan_gemm_all_gather(fviews[0].geometry(), FU_W, 0, 1, fa[0], FU_K, fb, FU_K, fu_off, FU_M,
+                                          FU_N, FU_K, FU_DTYPE)
 
     # ---------------- warm-up and timed regions: the all-gather job K times, then the fused job K
     # times, each region bracketed by device synchronisation; a step is one of each
@@ -428,8 +484,8 @@ def main() -> int:
                                "step_ms_min": round(runs[0], 5), "step_ms_max": round(runs[-1], 5)}
         return per_step, wall
 
-    copy_ms, wall_copy = timed(copy_job, blocks=3) if args.only != "fused" else (0.0, 0.0)
-    fused_ms, wall_fused = timed(fused_job, blocks=3) if (fused_ok and args.only != "copy") else (0.0, 0.0)
+    copy_ms, wall_copy = timed(copy_job, blocks=3) if head is not None else (0.0, 0.0)
+    fused_ms, wall_fused = timed(fused_job, blocks=3) if fused_ok else (0.0, 0.0)
     step_ms = copy_ms + fused_ms
     wall = wall_copy + wall_fused
     if args.calib_copy_mib > 0:
@@ -440,13 +496,9 @@ def main() -> int:
         del src, dst
 
     # ---------------- rates and rooflines
-    per_call_bytes = ag_plan.bytes_read + ag_plan.bytes_written          # (1+W) * M_local * N * e
-    copy_launch_s = max(copy_ms, 1e-9) / 1e3 / AG_W     # profiling runs with --only fused time no copy
-    copy_gbs = AG_W * per_call_bytes / (max(copy_ms, 1e-9) / 1e3) / 1e9
-    traffic = _traffic(f"ag_copy_kernel_w8_{AG_M}x{AG_N}_f16_pmc.md", "ag_copy.hip", per_call_bytes)
     out = {
         "metric": METRIC,
-        "value": round(copy_gbs, 2),
+        "value": None,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -458,33 +510,40 @@ def main() -> int:
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": f"all-gather W={AG_W} logical ranks, {AG_M}x{AG_N} fp16 per rank, tile "
-                        f"{AG_TILE[0]}x{AG_TILE[1]}, {AG_PROGRAMS} programs (8 calls per step)"
+            "workload": (f"all-gather W={AG_W} logical ranks, {AG_M}x{AG_N} fp16 per rank, tile "
+                         f"{AG_TILE[0]}x{AG_TILE[1]}, {AG_PROGRAMS} programs (8 calls per step)"
+                         if head is not None else "")
                         + (f" + fused GEMM+all-gather W={FU_W}, M_local={FU_M} K={FU_K} N={FU_N} fp16 "
                            f"(8 calls per step)" if fused_ok else ""),
             "parallelism": "one GPU; W logical ranks are heap regions",
         },
-        "roofline": {
+        "device": {"name": dev_props.name, "cus": dev_props.multi_processor_count},
+        "wall_s_timed": round(wall, 4),
+    }
+    if head is not None:
+        per_call_bytes = ag_plan.bytes_read + ag_plan.bytes_written          # (1+W) * M_local * N * e
+        copy_launch_s = copy_ms / 1e3 / AG_W
+        copy_gbs = AG_W * per_call_bytes / (copy_ms / 1e3) / 1e9
+        out["value"] = round(copy_gbs, 2)
+        out["roofline"] = {
             "bound": "hbm",
             "achieved": round(per_call_bytes / copy_launch_s / 1e9, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(per_call_bytes / copy_launch_s / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
+            "traffic": _traffic(f"ag_copy_kernel_w8_{AG_M}x{AG_N}_f16_pmc.md", "ag_copy.hip", per_call_bytes),
             "kernel": f"ag_copy_kernel<VEC={ag_plan.vec_bytes},W={AG_W},VPT={ag_plan.vectors_per_thread}>",
             "alg_bytes_per_launch": per_call_bytes,
             "avg_launch_us": round(copy_launch_s * 1e6, 3),
-        },
-        "spread": spread.get(id(copy_job)),
-        "device": {"name": dev_props.name, "cus": dev_props.multi_processor_count},
-        "plan_all_gather": {k: ag_plan.as_dict()[k] for k in ("vec_bytes", "n_programs", "threads", "total_tiles",
-                                                              "vectors_per_thread")},
-        "wall_s_timed": round(wall, 4),
-    }
+        }
+        out["spread"] = spread.get(id(copy_job))
+        out["plan_all_gather"] = {k: ag_plan.as_dict()[k] for k in ("vec_bytes", "n_programs", "threads",
+                                                                    "total_tiles", "vectors_per_thread")}
+        out["copy_ms_per_job"] = round(copy_ms, 5)
     if fused_ok:
         flops = fu_plan.flops
-        fu_launch_s = max(fused_ms, 1e-9) / 1e3 / FU_W
-        fu_tflops = FU_W * flops / (max(fused_ms, 1e-9) / 1e3) / 1e12
+        fu_launch_s = fused_ms / 1e3 / FU_W
+        fu_tflops = FU_W * flops / (fused_ms / 1e3) / 1e12
         out["fused"] = {
             "metric": "fused GEMM+all-gather TFLOP/s",
             "value": round(fu_tflops, 2),
@@ -505,21 +564,25 @@ def main() -> int:
                                                        "total_tiles")},
             "spread": spread.get(id(fused_job)),
         }
-    out["copy_ms_per_job"] = round(copy_ms, 5)
     if not args.no_context and args.only == "all":
-        out["context"] = _context(args, stream, timed, views, ins, geom)
+        out["context"] = _context(args, stream, timed, head)
         out["context"]["fused"] = _context_fused(args, stream, timed, fviews, fu_off)
         out["context"]["calibration"] = _calibration(stream)
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = _cpu_baseline_copy(args.cpu_seconds)
+        if head is not None:
+            host_in = head.ins[0].cpu().numpy()
+            out["cpu_baseline"] = _cpu_baseline_copy(args.cpu_seconds, host_in)
+            del host_in
         if fused_ok:
             out["fused"]["cpu_baseline"] = _cpu_baseline_fused(args.cpu_seconds)
     print(json.dumps(out), flush=True)
-    for v in views + fviews:
-        v.destroy()
-    heap.destroy()
-    fheap.destroy()
+    if head is not None:
+        head.close()
+    if fused_ok:
+        for v in fviews:
+            v.destroy()
+        fheap.destroy()
     return 0
 
 

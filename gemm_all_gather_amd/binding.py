@@ -91,6 +91,8 @@ _SIGNATURES = {
     "ag_heap_rank_ptr": [_vp, _c_int, _c_size, ctypes.POINTER(ctypes.c_void_p)],
     "ag_heap_base_table": [_vp, ctypes.POINTER(ctypes.c_void_p)],
     "ag_heap_geometry": [_vp, ctypes.POINTER(Geometry)],
+    "ag_heap_info": [_vp, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                     ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_void_p)],
     "ag_all_gather": [_vp, _c_int, _c_int, _c_int, _vp, _c_size, _c_i64, _c_i64, _c_int, _c_int, _c_int,
                       _c_int, _vp],
     "ag_plan_all_gather": [ctypes.POINTER(Geometry), _c_int, _c_int, _c_int, _c_u64, _c_size, _c_i64, _c_i64,
@@ -243,6 +245,13 @@ class Heap:
         g = Geometry()
         _check(lib().ag_heap_geometry(self.handle, ctypes.byref(g)), "ag_heap_geometry")
         return g
+
+    def info(self) -> dict:
+        """ag_heap_info: n_ranks, rank (-1 for the root handle), bytes_per_rank, base_table (device address)."""
+        n, r, s, t = ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t(), ctypes.c_void_p()
+        _check(lib().ag_heap_info(self.handle, ctypes.byref(n), ctypes.byref(r), ctypes.byref(s), ctypes.byref(t)),
+               "ag_heap_info")
+        return {"n_ranks": n.value, "rank": r.value, "bytes_per_rank": s.value, "base_table": t.value or 0}
 
 
 def plan_all_gather(geom: Geometry, W, rank_start, rank_stride, input_addr, out_offset, M_local, N, dtype,

@@ -350,6 +350,18 @@ ag_status_t ag_heap_geometry(const ag_heap_t* heap, ag_heap_geometry_t* geom)
     return ok();
 }
 
+ag_status_t ag_heap_info(const ag_heap_t* heap, int* n_ranks, int* rank, size_t* bytes_per_rank,
+                         const uint64_t** dev_base_table)
+{
+    if (!heap) return fail(AG_ERR_INVALID_ARG, "heap is NULL");
+    const HeapCore& c = *heap->core;
+    if (n_ranks) *n_ranks = c.n_ranks;
+    if (rank) *rank = heap->rank;
+    if (bytes_per_rank) *bytes_per_rank = static_cast<size_t>(c.bytes_per_rank);
+    if (dev_base_table) *dev_base_table = c.table;
+    return ok();
+}
+
 // ---------------------------------------------------------------------------
 // all-gather (default, grouped, partitioned) and all-to-all: one planner
 // ---------------------------------------------------------------------------

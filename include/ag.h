@@ -165,6 +165,24 @@ ag_status_t ag_heap_base_table(const ag_heap_t* heap, const uint64_t** dev_table
 /* Geometry of a handle (host copy, no device access). */
 ag_status_t ag_heap_geometry(const ag_heap_t* heap, ag_heap_geometry_t* geom);
 
+/* What a device kernel needs to reach every rank's heap (ROCm/iris #591,
+ * "Hoist the peer heap bases": the context knows its rank and keeps the
+ * heap bases of all ranks in one device array, heap_bases, which the kernels
+ * read).  Host-only, no device access:
+ *   *n_ranks         number of regions (ranks) of the heap;
+ *   *rank            the calling rank of a view (ag_heap_view), -1 for the
+ *                    root handle;
+ *   *bytes_per_rank  region stride in bytes (region r starts at
+ *                    heap_bases[r] = region 0 + r*bytes_per_rank);
+ *   *dev_base_table  device address of heap_bases, uint64_t[n_ranks], owned
+ *                    by the heap (valid until its last handle is destroyed;
+ *                    the caller must not write or free it).
+ * Each output pointer may be NULL, and that item is then not reported.
+ * AG_ERR_INVALID_ARG when heap is NULL.  The same values as
+ * ag_heap_geometry (n_ranks, rank, bytes_per_rank) and ag_heap_base_table. */
+ag_status_t ag_heap_info(const ag_heap_t* heap, int* n_ranks, int* rank, size_t* bytes_per_rank,
+                         const uint64_t** dev_base_table);
+
 /* ------------------------------------------------------------------------
  * All-gather (ROCm/iris #626 "Summary" and "Triton CCL all-gather"; result
  * defined by ROCm/iris #594 "Multi-GPU CI").

@@ -12,6 +12,7 @@ from .ag_oracle import (  # noqa: F401
     F32,
     ELEM_BYTES,
     all_gather_oracle,
+    store_to_members,
     all_gather_expected_block,
     group_members,
     all_to_all_oracle,
@@ -21,6 +22,8 @@ from .ag_oracle import (  # noqa: F401
     f16_bits_to_f64,
     bf16_bits_to_f64,
     decode_bits,
+    gemm_exact,
+    gemm_exact_entries,
     gemm_oracle,
     gemm_oracle_entries,
     gemm_all_gather_oracle,

@@ -90,14 +90,26 @@ def all_gather_oracle(slab: np.ndarray, region_bytes: int, inputs: list[np.ndarr
     out = slab.copy()
     world = len(inputs)
     members = group_members(rank_start, rank_stride, world)
-    blocks = [np.ascontiguousarray(x).view(np.uint8).reshape(-1) for x in inputs]
-    for h in members:
-        cursor = h * region_bytes + out_offset
-        for j in range(world):
-            n = blocks[j].size
-            out[cursor:cursor + n] = blocks[j]
-            cursor += n
+    regions = [out[h * region_bytes:(h + 1) * region_bytes] for h in members]
+    cursor = out_offset
+    for j in range(world):
+        block = np.ascontiguousarray(inputs[j]).view(np.uint8).reshape(-1)
+        store_to_members(regions, cursor, block)     # group rank j's rows follow ranks 0..j-1
+        cursor += block.size
     return out
+
+
+def store_to_members(regions: list[np.ndarray], offset: int, data: np.ndarray) -> None:
+    """Write the same bytes at the same offset of every member's region (in place).
+
+    One rank's all-gather is this store with its input at
+    out_offset + g*M_local*N*e (ROCm/iris #626, "Summary": the tile is stored
+    to every rank's heap at the same symmetric offset).  regions are uint8
+    arrays (views into the heap), data a uint8 array.
+    """
+    n = data.size
+    for region in regions:
+        np.copyto(region[offset:offset + n], data)
 
 
 # ---------------------------------------------------------------------------
@@ -243,28 +255,36 @@ def _logical_b(b_bits: np.ndarray, dtype: str, b_layout: str) -> np.ndarray:
     raise ValueError(f"b_layout must be 'kn' or 'nk', got {b_layout!r}")
 
 
-def gemm_oracle(a_bits: np.ndarray, b_bits: np.ndarray, dtype: str, b_layout: str = "nk") -> np.ndarray:
-    """C = A . B rounded once to the 16-bit dtype; returns uint16 bits of shape (M, N).
+def gemm_exact(a_bits: np.ndarray, b_bits: np.ndarray, dtype: str, b_layout: str = "nk") -> np.ndarray:
+    """The float64 product A . B of 16-bit operands, before any rounding to the output type; (M, N).
 
-    ROCm/iris #626, "Assembly" table and "Benchmark": the matmul produces an
-    fp16 C tile from fp16 operands.  The products and sums are formed in
-    float64 and rounded once (round-to-nearest-even) to the output type.
-    a_bits is the row-major (M, K) A.
+    Each product of two 16-bit values is exact in float64; the sums carry
+    float64 rounding only, far below the output type's resolution.  This is
+    the value gemm_oracle rounds, and the "exact" value against which a
+    float32-accumulating kernel's error is measured.  a_bits is the row-major
+    (M, K) A.
     """
     a = decode_bits(a_bits, dtype)
     b = _logical_b(b_bits, dtype, b_layout)
     if a.shape[1] != b.shape[0]:
         raise ValueError(f"inner dimensions differ: A is {a.shape}, B is {b.shape}")
-    c = np.matmul(a, b)
-    return _encode(c, dtype)
+    return np.matmul(a, b)
 
 
-def gemm_oracle_entries(a_bits: np.ndarray, b_bits: np.ndarray, dtype: str, rows, cols,
-                        b_layout: str = "nk") -> np.ndarray:
-    """Selected entries C[rows[i], cols[i]] of gemm_oracle, each one as its own float64 dot product.
+def gemm_oracle(a_bits: np.ndarray, b_bits: np.ndarray, dtype: str, b_layout: str = "nk") -> np.ndarray:
+    """C = A . B rounded once to the 16-bit dtype; returns uint16 bits of shape (M, N).
 
-    For full-size checks where the whole product is too slow on the CPU.
+    ROCm/iris #626, "Assembly" table and "Benchmark": the matmul produces an
+    fp16 C tile from fp16 operands.  The products and sums are formed in
+    float64 (gemm_exact) and rounded once (round-to-nearest-even) to the
+    output type.
     """
+    return _encode(gemm_exact(a_bits, b_bits, dtype, b_layout), dtype)
+
+
+def gemm_exact_entries(a_bits: np.ndarray, b_bits: np.ndarray, dtype: str, rows, cols,
+                       b_layout: str = "nk") -> np.ndarray:
+    """Selected entries C[rows[i], cols[i]] of gemm_exact, each one as its own float64 dot product."""
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
     a = np.asarray(a_bits, dtype=np.uint16)
@@ -274,7 +294,16 @@ def gemm_oracle_entries(a_bits: np.ndarray, b_bits: np.ndarray, dtype: str, rows
         a_row = decode_bits(a[r, :], dtype)
         b_col = decode_bits(b[c, :] if b_layout == "nk" else b[:, c], dtype)
         vals[i] = np.dot(a_row, b_col)
-    return _encode(vals, dtype)
+    return vals
+
+
+def gemm_oracle_entries(a_bits: np.ndarray, b_bits: np.ndarray, dtype: str, rows, cols,
+                        b_layout: str = "nk") -> np.ndarray:
+    """Selected entries C[rows[i], cols[i]] of gemm_oracle, each one as its own float64 dot product.
+
+    For full-size checks where the whole product is too slow on the CPU.
+    """
+    return _encode(gemm_exact_entries(a_bits, b_bits, dtype, rows, cols, b_layout), dtype)
 
 
 def gemm_all_gather_oracle(slab: np.ndarray, region_bytes: int, a_list, b_list, dtype: str,

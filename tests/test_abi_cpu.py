@@ -243,6 +243,15 @@ def test_heap_create_without_device_reports_hip_error():
     assert got == ag.AG_ERR_HIP and "hip" in msg.lower()
 
 
+def test_heap_info_rejects_a_null_handle():
+    l = ag.lib()
+    n, r, s, t = ctypes.c_int(7), ctypes.c_int(7), ctypes.c_size_t(7), ctypes.c_void_p(7)
+    st = l.ag_heap_info(None, ctypes.byref(n), ctypes.byref(r), ctypes.byref(s), ctypes.byref(t))
+    assert st == ag.AG_ERR_INVALID_ARG and "heap" in l.ag_last_error_message().decode()
+    # nothing is written on failure
+    assert (n.value, r.value, s.value, t.value) == (7, 7, 7, 7)
+
+
 def test_heap_argument_validation_without_device():
     assert status_of(ag.Heap.create, 0, MiB)[0] == ag.AG_ERR_INVALID_ARG
     assert status_of(ag.Heap.create, 2, 0)[0] == ag.AG_ERR_INVALID_ARG

@@ -20,8 +20,27 @@ pytestmark = pytest.mark.gpu
 E = {"f16": 2, "bf16": 2, "f32": 4}
 
 
+def _accepted_tile(th, dev, W, start, stride, out_offset, M, N, dtype, tiles, n_programs):
+    """The first tile of the candidates that the planner accepts for every member's call.
+
+    The vector width, and so the set of tiles a call supports, follows the alignment of the input and of
+    each member's row block; a case only counts when every call launches a kernel.
+    """
+    for tile in tiles:
+        try:
+            for j in range(W):
+                v = th.view(start + j * stride)
+                ag.plan_all_gather(v.geometry(), W, start, stride, dev[j], out_offset, M, N, dtype, tile[0],
+                                   tile[1], n_programs)
+            return tile
+        except ag.AgError as exc:
+            assert exc.status == ag.AG_ERR_UNSUPPORTED and "vectors" in exc.message, exc
+    raise AssertionError(f"no candidate tile is accepted: {tiles}")
+
+
 def _case(R, S, W, start, stride, M, N, dtype, out_offset, tile=(0, 0), n_programs=0, seed=0,
           bits=False, fill_random=False):
+    """tile: one (tile_m, tile_n), or a list of candidates (the first one every call accepts runs)."""
     require_gpu()
     log(f"all_gather R={R} S={S} W={W} group=({start},{stride}) M={M} N={N} {dtype} off={out_offset} "
         f"tile={tile} programs={n_programs} seed={seed}")
@@ -33,6 +52,9 @@ def _case(R, S, W, start, stride, M, N, dtype, out_offset, tile=(0, 0), n_progra
         else:
             ins = [gen.uniform_pm1((M, N), dtype, seed, j) for j in range(W)]
         dev = [to_device(x) for x in ins]
+        if isinstance(tile, list):
+            tile = _accepted_tile(th, dev, W, start, stride, out_offset, M, N, dtype, tile, n_programs)
+            log(f"  tile {tile}")
         run_all_gather(th, dev, W, start, stride, out_offset, M, N, dtype, tile[0], tile[1], n_programs)
         got = th.host()
         want = all_gather_oracle(before, S, ins, start, stride, out_offset)
@@ -73,15 +95,14 @@ def test_tiny_sweep(W, start, stride, M, N):
     tiles = [(8, 256), (1, 256), (4, 64), (16, 128), (2, 512), (32, 64)]
     if e == 4:
         tiles = [(8, 256), (1, 512), (4, 64), (16, 128), (2, 512)]
-    tile = tiles[int(rng.integers(0, len(tiles)))]
+    first = int(rng.integers(0, len(tiles)))
+    # the drawn tile first; where the call's vector width rules it out, the next one the planner accepts
+    # (8x256 holds 256 to 2048 vectors at every width, so some tile always runs)
+    tiles = tiles[first:] + tiles[:first] + [(8, 256)]
     programs = [1, 3, 4, 7, 64, 10_000][int(rng.integers(0, 6))]
     out_offset = int(rng.integers(0, 40)) * e          # often unaligned to 16 bytes
     S = ((out_offset + W * M * N * e + 300) // 256 + 1) * 256
-    try:
-        _case(8, S, W, start, stride, M, N, dtype, out_offset, tile, programs, seed=W * 1000 + M)
-    except ag.AgError as exc:
-        # a tile with too few or too many vectors for the chosen width is rejected, never run
-        assert exc.status == ag.AG_ERR_UNSUPPORTED and "vectors" in exc.message, exc
+    _case(8, S, W, start, stride, M, N, dtype, out_offset, tiles, programs, seed=W * 1000 + M)
 
 
 @pytest.mark.parametrize("n_programs", [64, 128, 256])
@@ -198,6 +219,13 @@ def test_library_owned_heap_create_and_alloc():
 
         table.copy_(torch.as_tensor(_T(), device="cuda"))
         assert table.cpu().tolist() == [g.slab_addr + r * g.bytes_per_rank for r in range(R)]
+        # ag_heap_info reports what ag_heap_geometry and ag_heap_base_table report, for the root and views
+        for h in [heap] + views:
+            info, hg = h.info(), h.geometry()
+            assert info == {"n_ranks": hg.n_ranks, "rank": hg.rank, "bytes_per_rank": hg.bytes_per_rank,
+                            "base_table": h.base_table()}
+        assert heap.info()["rank"] == -1 and [v.info()["rank"] for v in views] == list(range(W))
+        assert len({v.info()["base_table"] for v in views} | {heap.info()["base_table"]}) == 1
         for v in views:
             v.destroy()
     finally:

@@ -16,15 +16,13 @@ import torch
 
 from gemm_all_gather_amd import binding as ag
 from gemm_all_gather_amd import inputs as gen
-from oracle import (gemm_all_gather_oracle, gemm_oracle, gemm_oracle_entries, all_gather_oracle,
-                    decode_bits, group_members)
+from oracle import gemm_all_gather_oracle, decode_bits
+from tests.fused_check import MAX_ABS, check_entries, check_full, tile_samples
 from tests.gpu_util import TorchHeap, log, require_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
 TILES = [(256, 256, 64), (256, 224, 64), (128, 128, 64), (0, 0, 0)]
-MAX_ABS = 2e-2
-MAX_REL = 1e-2
 
 
 def _run_fused(th, a_dev, b_dev, W, start, stride, off, M, N, K, dtype, tile, programs=0, stream=None):
@@ -70,31 +68,6 @@ def test_integer_operands_bit_exact(M, N, K, tile, dtype):
         th.close()
 
 
-def _check_tolerance(got_bits, a_bits, b_bits, dtype, exact=None, max_abs=MAX_ABS):
-    """Tolerance and rigorous fp32-accumulation bound against the float64 product.
-
-    max_abs=None skips the absolute bar: with unit-variance C, bf16's own
-    rounding (half an ulp is 2^-8 |C|) exceeds 2e-2 once |C| > 5.
-    """
-    A = decode_bits(a_bits, dtype)
-    B = decode_bits(b_bits, dtype)
-    if exact is None:
-        exact = A @ B.T
-    got = decode_bits(got_bits, dtype)
-    K = A.shape[1]
-    err = np.abs(got - exact)
-    assert np.all(np.isfinite(got))
-    if max_abs is not None:
-        assert err.max() <= max_abs, f"max abs error {err.max()}"
-    rel = np.linalg.norm(got - exact) / max(np.linalg.norm(exact), 1e-300)
-    assert rel <= MAX_REL, f"relative error {rel}"
-    # |fl32(sum) - exact| <= K u32 sum|a||b|; the final rounding adds at most one ulp of the output type
-    ulp = (2.0 ** -10 if dtype == "f16" else 2.0 ** -7) * np.maximum(np.abs(exact), 2.0 ** -14)
-    bound = ulp + 2 * K * 2.0 ** -24 * (np.abs(A) @ np.abs(B).T)
-    assert np.all(err <= bound), f"{np.count_nonzero(err > bound)} entries outside the fp32 bound"
-    return err.max(), rel
-
-
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("scale_a", ["scaled", "unit"])
@@ -114,8 +87,10 @@ def test_random_operands_within_tolerance(dtype, tile, scale_a):
         for r in range(W):
             for j in range(W):
                 out = host[r * S + j * blk:r * S + (j + 1) * blk].view(np.uint16).reshape(M, N)
-                _check_tolerance(out, a[j], b[j], dtype,
-                                 max_abs=None if (scale_a == "unit" and dtype == "bf16") else MAX_ABS)
+                # with unit-variance C, bf16's own rounding (half an ulp is 2^-8 |C|) exceeds 2e-2 once |C| > 5
+                check_full(out, a[j], b[j], dtype,
+                           max_abs=None if (scale_a == "unit" and dtype == "bf16") else MAX_ABS,
+                           what=f"region {r} rank {j}")
                 if scale_a == "unit":
                     assert np.abs(decode_bits(out, dtype)).max() > 0.5     # non-trivial output
     finally:
@@ -193,15 +168,87 @@ def test_fused_validation_on_launching_entry_point():
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads (the benchmark's launch configuration: tiles and programs chosen by the library)
+# many tiles per program over full groups of the grouped tile order, bit-exact
 # ---------------------------------------------------------------------------
 
-def _full_size(M, N, K, dtype, seed, samples=1500):
+# (tile, programs): 256x224 gives 10 x 3 tiles at M=2400, N=464 (8 tile rows of the grouped order, then a
+# ragged group of 2), 128x128 gives 19 x 4 (8 + 8 + 3), 256x256 gives 10 x 2; the program counts give each
+# program 4 to 10 tiles, with and without the XCD renumbering (counts that are multiples of 8), and one tile
+# per program at 256
+MANY_TILES = [((256, 224, 64), 6), ((256, 224, 64), 8), ((128, 128, 64), 8), ((128, 128, 64), 16),
+              ((128, 128, 64), 19), ((256, 256, 64), 5), ((256, 224, 64), 256), ((0, 0, 0), 0)]
+
+
+@pytest.mark.parametrize("tile,programs", MANY_TILES)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_integer_operands_many_tiles_per_program_bit_exact(tile, programs, dtype):
     require_gpu()
-    W = 8
+    M, N, K, W = 2400, 464, 128, 8
+    lo, hi = (-3, 3) if dtype == "f16" else (-2, 2)     # every partial sum an integer below 2^24
+    off = 1024
+    log(f"fused int many tiles M={M} N={N} K={K} tile={tile} programs={programs} {dtype} W={W}")
+    a = [gen.small_integers((M, K), dtype, lo, hi, 21, j) for j in range(W)]
+    b = [gen.small_integers((N, K), dtype, lo, hi, 22, j) for j in range(W)]
+    S = _region_size(W, M, N, off)
+    th = TorchHeap(8, S)
+    try:
+        if tile != (0, 0, 0):
+            p = ag.plan_gemm_all_gather(th.view(0).geometry(), W, 0, 1, 1 << 40, K, 1 << 41, K, off, M, N, K, dtype,
+                                        tile[0], tile[1], tile[2], programs)
+            assert p.tiles_m >= 9                                   # full 8-row groups plus a ragged one
+            if programs < 256:
+                assert -(-p.total_tiles // p.n_programs) >= 4            # the busiest program walks >= 4 tiles
+        before = th.host()
+        _run_fused(th, [to_device(x) for x in a], [to_device(x) for x in b], W, 0, 1, off, M, N, K, dtype, tile,
+                   programs)
+        got = th.host()
+        want = gemm_all_gather_oracle(before, S, a, b, dtype, 0, 1, off)
+        if not np.array_equal(got, want):
+            bad = np.flatnonzero(got != want)
+            raise AssertionError(f"{bad.size} bytes differ, first at region {bad[0] // S} offset {bad[0] % S}")
+    finally:
+        th.close()
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads (the benchmark's launch configuration: tiles and programs chosen by the library,
+# and the 256x256 tile of the pages' fused kernel)
+# ---------------------------------------------------------------------------
+
+def _full_size_heap(th, W, blk, guard):
+    """Every member region identical, guards untouched, no output word left at the fill pattern, all finite."""
+    sentinel = torch.tensor([int(np.uint16(gen.SENTINEL16).view(np.int16))], device="cuda", dtype=torch.int16)
+    ref_region = th.region(0)[guard:guard + W * blk]
+    for r in range(W):
+        reg = th.region(r)
+        assert torch.equal(reg[guard:guard + W * blk], ref_region), f"region {r} differs from region 0"
+        assert torch.all(reg[:guard].view(torch.int16) == sentinel), f"guard before region {r}'s output"
+        assert torch.all(reg[guard + W * blk:].view(torch.int16) == sentinel), f"guard after region {r}'s output"
+    words = ref_region.view(torch.int16)
+    assert not torch.any(words == sentinel), "an output word still holds the fill pattern (unwritten entry)"
+    return ref_region
+
+
+_INPUTS = {}
+
+
+def _inputs(M, N, K, dtype, seed, W=8):
+    """Seeded operands, cached across the full-size cases of one shape (N(0,1)/sqrt(K) on A and B)."""
+    key = (M, N, K, dtype, seed)
+    if key not in _INPUTS:
+        _INPUTS.clear()
+        a = [gen.normal_scaled((M, K), dtype, K ** -0.5, seed, j) for j in range(W)]
+        b = gen.normal_scaled((N, K), dtype, K ** -0.5, seed, 99)
+        _INPUTS[key] = (a, b)
+    return _INPUTS[key]
+
+
+def test_full_size_m1024_fp16_every_element():
+    """M_local 1024 (fused context workload): every element of every rank's C_j against the oracle."""
+    require_gpu()
+    M, N, K, W, dtype = 1024, 3584, 8192, 8, "f16"
     log(f"full-size fused W=8 M_local={M} N={N} K={K} {dtype}: generating inputs")
-    a = [gen.normal_scaled((M, K), dtype, K ** -0.5, seed, j) for j in range(W)]
-    b = gen.normal_scaled((N, K), dtype, K ** -0.5, seed, 99)
+    a, b = _inputs(M, N, K, dtype, 40)
     a_dev = [to_device(x) for x in a]
     b_dev = to_device(b)
     blk = M * N * 2
@@ -212,44 +259,48 @@ def _full_size(M, N, K, dtype, seed, samples=1500):
         log("  running")
         _run_fused(th, a_dev, [b_dev] * W, W, 0, 1, guard, M, N, K, dtype, (0, 0, 0))
         torch.cuda.synchronize()
-        sentinel = torch.tensor([int(np.uint16(gen.SENTINEL16).view(np.int16))], device="cuda", dtype=torch.int16)
-        ref_region = th.region(0)[guard:guard + W * blk]
-        for r in range(W):
-            reg = th.region(r)
-            assert torch.equal(reg[guard:guard + W * blk], ref_region), f"region {r} differs from region 0"
-            assert torch.all(reg[:guard].view(torch.int16) == sentinel)
-            assert torch.all(reg[guard + W * blk:].view(torch.int16) == sentinel)
+        ref_region = _full_size_heap(th, W, blk, guard)
         out = ref_region.cpu().numpy().view(np.uint16).reshape(W * M, N)
-        rng = np.random.default_rng(seed)
+        log("  comparing every element with the oracle")
         worst = 0.0
         for j in range(W):
-            rows = rng.integers(0, M, samples)
-            cols = rng.integers(0, N, samples)
-            rows[:4] = [0, M - 1, 0, M - 1]
-            cols[:4] = [0, N - 1, N - 1, 0]
-            want = gemm_oracle_entries(a[j], b, dtype, rows, cols, "nk")
-            got = out[j * M + rows, cols]
-            A = decode_bits(a[j][rows], dtype)
-            Bc = decode_bits(b[cols], dtype)
-            exact = np.einsum("ik,ik->i", A, Bc)
-            g = decode_bits(got, dtype)
-            err = np.abs(g - exact)
-            worst = max(worst, err.max())
-            assert err.max() <= MAX_ABS
-            ulp = (2.0 ** -10 if dtype == "f16" else 2.0 ** -7) * np.maximum(np.abs(exact), 2.0 ** -14)
-            bound = ulp + 2 * K * 2.0 ** -24 * np.einsum("ik,ik->i", np.abs(A), np.abs(Bc))
-            assert np.all(err <= bound)
-            # the oracle's rounded value and the GPU's differ by at most one output ulp
-            assert np.all(np.abs(decode_bits(want, dtype) - g) <= ulp + bound)
-        log(f"  max abs error over samples {worst:.3e}")
+            err, rel = check_full(out[j * M:(j + 1) * M], a[j], b, dtype, what=f"rank {j}")
+            worst = max(worst, err)
+        log(f"  max abs error {worst:.3e}")
     finally:
         th.close()
 
 
-def test_full_size_m1024_fp16():
-    _full_size(1024, 3584, 8192, "f16", 40)
-
-
+@pytest.mark.parametrize("tile", [(0, 0, 0), (256, 256, 64)])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_full_size_m16384(dtype):
-    _full_size(16384, 3584, 8192, dtype, 41)
+def test_full_size_m16384(dtype, tile):
+    """M_local 16384: the four corners and one interior entry of every output tile of every rank."""
+    require_gpu()
+    M, N, K, W = 16384, 3584, 8192, 8
+    log(f"full-size fused W=8 M_local={M} N={N} K={K} {dtype} tile={tile}: generating inputs")
+    a, b = _inputs(M, N, K, dtype, 41)
+    a_dev = [to_device(x) for x in a]
+    b_dev = to_device(b)
+    blk = M * N * 2
+    guard = 1 << 20
+    S = W * blk + 2 * guard
+    th = TorchHeap(W, S)
+    try:
+        p = ag.plan_gemm_all_gather(th.view(0).geometry(), W, 0, 1, a_dev[0], K, b_dev, K, guard, M, N, K, dtype,
+                                    *tile, 0)
+        log(f"  running ({p.tile_m}x{p.tile_n} tiles, {p.n_programs} programs)")
+        _run_fused(th, a_dev, [b_dev] * W, W, 0, 1, guard, M, N, K, dtype, tile)
+        torch.cuda.synchronize()
+        ref_region = _full_size_heap(th, W, blk, guard)
+        out = ref_region.cpu().numpy().view(np.uint16).reshape(W * M, N)
+        rng = np.random.default_rng([41, p.tile_m, p.tile_n])
+        worst = 0.0
+        for j in range(W):
+            rows, cols = tile_samples(M, N, p.tile_m, p.tile_n, rng)
+            err, _ = check_entries(out[j * M + rows, cols], a[j], b, dtype, rows, cols, what=f"rank {j}")
+            worst = max(worst, err)
+        log(f"  {rows.size} entries per rank, max abs error {worst:.3e}")
+    finally:
+        th.close()
+        del a_dev, b_dev
+        torch.cuda.empty_cache()

@@ -181,6 +181,102 @@ def test_all_to_all_kernel_hoists_bases_and_pipelines_tiles(asm, vec, w, vpt):
     assert _meta(asm["ag_copy.hip"], sym)["scratch"] == 0
 
 
+_SIGN_OPS = ("s_ashr_i32", "s_ashr_i64", "s_bfe_i32", "s_bfe_i64", "s_sext_i32_i8", "s_sext_i32_i16",
+             "v_ashrrev_i32", "v_ashrrev_i64", "v_bfe_i32")
+
+
+def _sregs(tok):
+    m = re.match(r"s\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"s(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _sign_extended_lane_reads(lines):
+    """Instructions that sign-propagate a 32-bit half read out of a lane (v_readlane / v_readfirstlane).
+
+    A 64-bit address assembled from two 32-bit halves must zero-extend its low
+    half; a sign extension (s_ashr / s_bfe_i* / sext of that register) turns
+    the upper word into all ones whenever bit 31 of the low half is set.
+    Checked from the first lane read to the first store.
+    """
+    halves, bad, seen = set(), [], False
+    for ln in lines:
+        if ln.startswith("buffer_store") or ln.startswith("global_store"):
+            if seen:
+                break
+        m = re.match(r"v_read(?:first)?lane_b32\s+(s\d+)", ln)
+        if m:
+            halves |= _sregs(m.group(1))
+            seen = True
+            continue
+        if not seen or " " not in ln:
+            continue
+        op, rest = ln.split(None, 1)
+        ops = [o.strip() for o in rest.split(",")]
+        dst = _sregs(ops[0])
+        if op.split("_e32")[0].split("_e64")[0] in _SIGN_OPS and any(_sregs(o) & halves for o in ops[1:]):
+            bad.append(ln)
+        halves -= dst                                  # a half overwritten by something else is no longer one
+    return bad
+
+
+@pytest.mark.parametrize("vec,w,vpt,part", COPY_CASES)
+def test_copy_kernel_bases_are_zero_extended(asm, vec, w, vpt, part):
+    """The 64-bit destination bases built from readlane halves never sign-extend a half."""
+    for wide in ("0", "1"):
+        pat = f"ag_copy_kernelILi{vec}ELi{w}ELi{vpt}ELi0ELb{part}ELb{wide}E"
+        if not re.search(r"^_Z\S*" + pat, asm["ag_copy.hip"], re.M):
+            continue
+        _, lines = _kernel_body(asm["ag_copy.hip"], pat)
+        assert sum(ln.startswith("v_readlane_b32") for ln in lines) >= 2 * int(w)
+        assert not _sign_extended_lane_reads(lines), _sign_extended_lane_reads(lines)
+
+
+@pytest.mark.parametrize("w,vpt", [("8", "2"), ("4", "1")])
+def test_all_to_all_bases_are_zero_extended(asm, w, vpt):
+    for wide in ("0", "1"):
+        _, lines = _kernel_body(asm["ag_copy.hip"], f"ag_a2a_kernelILi16ELi{w}ELi{vpt}ELb{wide}E")
+        assert not _sign_extended_lane_reads(lines), _sign_extended_lane_reads(lines)
+
+
+_LANE_BASE_SNIPPET = r"""
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+__global__ void zext_base(const uint64_t* t, uint64_t* out) {
+    const uint64_t v = t[threadIdx.x & 63];
+    const uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+    const uint64_t b = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(hi, 3))) << 32) |
+                       static_cast<uint32_t>(__builtin_amdgcn_readlane(lo, 3));
+    out[threadIdx.x] = b + 4096;
+}
+__global__ void sext_base(const uint64_t* t, uint64_t* out) {
+    const uint64_t v = t[threadIdx.x & 63];
+    const uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+    const uint64_t b = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(hi, 3))) << 32) |
+                       static_cast<uint64_t>(static_cast<int64_t>(__builtin_amdgcn_readlane(lo, 3)));
+    out[threadIdx.x] = b + 4096;
+}
+"""
+
+
+def test_sign_extension_check_catches_a_sign_extended_half(tmp_path):
+    """The checker itself, on a compiled snippet: a low half widened through int64_t is flagged, the
+    zero-extended one is not."""
+    src = tmp_path / "lane_base.hip"
+    src.write_text(_LANE_BASE_SNIPPET)
+    out = tmp_path / "lane_base.s"
+    subprocess.run([_hipcc(), "--offload-arch=gfx950", "-O3", "--cuda-device-only", "-S", "-o", str(out), str(src)],
+                   check=True, capture_output=True)
+    text = out.read_text()
+    _, good = _kernel_body(text, "zext_base")
+    _, bad = _kernel_body(text, "sext_base")
+    assert any(ln.startswith("v_readlane_b32") for ln in bad)
+    assert not _sign_extended_lane_reads(good)
+    assert _sign_extended_lane_reads(bad)
+
+
 # (tile, B N-contiguous): the 256x256 kernel takes B K-contiguous only
 GEMM_CFGS = [("256ELi224", "0"), ("256ELi224", "1"), ("256ELi256", "0"), ("128ELi128", "0"), ("128ELi128", "1")]
 
@@ -300,7 +396,11 @@ def test_report_registers(asm, capsys):
     assert rows
     # the instantiations the benchmark workloads run, then a summary over all of them
     bench = [r"ag_copy_kernelILi16ELi8ELi1ELi0ELb0ELb1E", r"ag_copy_kernelILi16ELi8ELi1ELi0ELb0ELb0E",
+             r"ag_copy_kernelILi16ELi8ELi2ELi0ELb0ELb1E",
+             r"ag_copy_kernelILi16ELi8ELi1ELi1ELb0ELb0E", r"ag_copy_kernelILi16ELi8ELi1ELi2ELb0ELb0E",
+             r"ag_copy_kernelILi16ELi8ELi1ELi4ELb0ELb0E", r"ag_copy_kernelILi16ELi1ELi1ELi0ELb1ELb1E",
              r"ag_a2a_kernelILi16ELi8ELi2ELb1E",
+             r"ag_gemm_kernelILb0ELi8E\S*CfgILi256ELi256E\S*ELb0EEEv", r"ag_gemm_kernelILb1ELi8E\S*CfgILi256ELi256E\S*ELb0EEEv",
              r"ag_gemm_kernelILb0ELi8E\S*CfgILi256ELi224E\S*ELb0EEEv", r"ag_gemm_kernelILb1ELi8E\S*CfgILi256ELi224E\S*ELb0EEEv",
              r"ag_gemm_kernelILb0ELi8E\S*CfgILi128ELi128E\S*ELb0EEEv", r"ag_gemm_kernelILb0ELi1E\S*CfgILi256ELi224E\S*ELb0EEEv",
              r"ag_gemm_kernelILb0ELi8E\S*CfgILi256ELi224E\S*ELb1EEEv", r"ag_gemm_kernelILb0ELi8E\S*CfgILi128ELi128E\S*ELb1EEEv"]

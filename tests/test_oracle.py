@@ -16,7 +16,7 @@ from oracle import (
     all_gather_oracle, all_gather_expected_block, group_members,
     all_to_all_oracle, all_to_all_expected_block,
     round_f64_to_f16_bits, round_f64_to_bf16_bits, f16_bits_to_f64, bf16_bits_to_f64,
-    gemm_oracle, gemm_oracle_entries, gemm_all_gather_oracle,
+    gemm_oracle, gemm_oracle_entries, gemm_all_gather_oracle, gemm_exact, gemm_exact_entries,
 )
 from gemm_all_gather_amd import inputs as gen
 
@@ -351,6 +351,30 @@ def test_gemm_within_float32_accumulation_bound(dtype):
     got = dec(gemm_oracle(a, b, dtype, "nk"))
     ulp_half = np.abs(exact) * (2.0 ** -11 if dtype == F16 else 2.0 ** -8) + 2.0 ** -24
     assert np.all(np.abs(got - exact) <= ulp_half)
+
+
+@pytest.mark.parametrize("dtype,lo,hi", [(F16, -3, 3), (BF16, -2, 2)])
+def test_gemm_exact_is_the_unrounded_product(dtype, lo, hi):
+    # K = 700 small integers: sums up to 6300 (fp16) / 2800 (bf16) are not representable in the output
+    # type, but the unrounded float64 product holds them exactly; brute force over Python integers
+    M, N, K = 4, 5, 700
+    a = gen.small_integers((M, K), dtype, lo, hi, 3, M, N, K)
+    b_nk = gen.small_integers((N, K), dtype, lo, hi, 4, M, N, K)
+    dec = f16_bits_to_f64 if dtype == F16 else bf16_bits_to_f64
+    ai = dec(a).astype(np.int64).tolist()
+    bi = dec(b_nk).astype(np.int64).T.tolist()
+    c = np.array(_int_matmul(ai, bi), dtype=np.float64)
+    got = gemm_exact(a, b_nk, dtype, "nk")
+    assert got.dtype == np.float64 and np.array_equal(got, c)
+    assert np.array_equal(gemm_exact(a, np.ascontiguousarray(b_nk.T), dtype, "kn"), c)
+    # clearing the sign bits gives sum |a||b|, the term of the float32 accumulation bound
+    absum = np.array(_int_matmul(np.abs(np.array(ai)).tolist(), np.abs(np.array(bi)).tolist()), dtype=np.float64)
+    assert np.array_equal(gemm_exact(a & 0x7FFF, b_nk & 0x7FFF, dtype, "nk"), absum)
+    # gemm_oracle is this product rounded once
+    enc = round_f64_to_f16_bits if dtype == F16 else round_f64_to_bf16_bits
+    assert np.array_equal(gemm_oracle(a, b_nk, dtype, "nk"), enc(c))
+    rows, cols = np.array([0, 3, 2, 1]), np.array([4, 0, 2, 1])
+    assert np.array_equal(gemm_exact_entries(a, b_nk, dtype, rows, cols, "nk"), c[rows, cols])
 
 
 def test_gemm_entries_match_full_product():
