@@ -194,11 +194,15 @@ class _Workload:
         self.ins = [_device_uniform(M * N, dtype, seed * 100 + i) for i in range(W)]
         self.geom = self.views[start].geometry()
 
-    def job(self, ag, stream, tile=(0, 0), programs=0, dest_group=0, schedule="tiles"):
+    def job(self, ag, stream, tile=(0, 0), programs=0, dest_group=0, schedule="tiles", tile_order="auto"):
         """All W members' calls, in group order."""
         def run():
             for i, r in enumerate(self.members):
-                if dest_group == 0 and schedule == "tiles":
+                if tile_order != "auto":
+                    ag.all_gather_ex(self.views[r], self.W, self.start, self.stride, self.ins[i], 0, self.M, self.N,
+                                     self.dtype, tile[0], tile[1], programs, dest_group, schedule, stream,
+                                     tile_order=tile_order)
+                elif dest_group == 0 and schedule == "tiles":
                     ag.all_gather(self.views[r], self.W, self.start, self.stride, self.ins[i], 0, self.M, self.N,
                                   self.dtype, tile[0], tile[1], programs, stream)
                 else:
@@ -206,9 +210,9 @@ class _Workload:
                                      self.dtype, tile[0], tile[1], programs, dest_group, schedule, stream)
         return run
 
-    def plan(self, ag, tile=(0, 0), programs=0):
-        return ag.plan_all_gather(self.geom, self.W, self.start, self.stride, self.ins[0], 0, self.M, self.N,
-                                  self.dtype, tile[0], tile[1], programs)
+    def plan(self, ag, tile=(0, 0), programs=0, tile_order="auto"):
+        return ag.plan_all_gather_ex(self.geom, self.W, self.start, self.stride, self.ins[0], 0, self.M, self.N,
+                                     self.dtype, tile[0], tile[1], programs, tile_order=tile_order)
 
     def close(self):
         import torch
@@ -223,7 +227,8 @@ class _Workload:
 def _context(args, stream, timed, head):
     """Context measurements beside the headline (each job = the group members' calls, timed like it).
 
-    * the 16384x8192 all-gather at 64/128/256 programs in fp16, bf16 and fp32;
+    * the 16384x8192 all-gather at 64/128/256 programs in fp16, bf16 and fp32, in the library's tile order
+      (tickets at this size) and in the fixed grid-stride order;
     * its variants: destination groups 1/2/4 and the partitioned schedule at 64/128/256 programs;
     * the 1024x4096 all-gather at 64/128/256 programs (75 MB per call: partly held by the last-level
       cache, so its rate exceeds what HBM sustains for the larger shape);
@@ -250,8 +255,16 @@ def _context(args, stream, timed, head):
         for P in (64, 128, 256):
             gb, ms = rate(wl, tile=AG_TILE, programs=P)
             p = wl.plan(ag, AG_TILE, P)
-            big[dt][str(P)] = {"GBs": gb, "frac": round(gb / HBM_PEAK_GBS, 4), "us_per_call": round(ms * 1e3 / wl.W, 2),
-                               "threads": p.threads, "vectors_per_thread": p.vectors_per_thread}
+            entry = {"GBs": gb, "frac": round(gb / HBM_PEAK_GBS, 4), "us_per_call": round(ms * 1e3 / wl.W, 2),
+                     "tile_order": {1: "stride", 2: "tickets"}[p.tile_order], "tiles_per_ticket": p.tiles_per_ticket,
+                     "threads": p.threads, "vectors_per_thread": p.vectors_per_thread}
+            if p.tile_order == ag.AG_ORDER_TICKETS:
+                # the same call with the fixed grid-stride tile order
+                gs, mss = rate(wl, tile=AG_TILE, programs=P, tile_order="stride")
+                entry["grid_stride_order"] = {"GBs": gs, "frac": round(gs / HBM_PEAK_GBS, 4),
+                                              "us_per_call": round(mss * 1e3 / wl.W, 2),
+                                              "threads": wl.plan(ag, AG_TILE, P, "stride").threads}
+            big[dt][str(P)] = entry
         if wl is not head:
             wl.close()
     ctx["all_gather_16384x8192"] = big
@@ -313,15 +326,18 @@ def _context(args, stream, timed, head):
 
 
 def _context_fused(args, stream, timed, views, fu_off):
-    """The fused workload at M_local 1024 (fp16), at M_local 16384 in bf16, and at M_local 16384 in fp16 with B
-    stored N-contiguous (a row-major K x N matrix), W=8, timed like the headline."""
+    """The fused workload at M_local 1024 (fp16), at M_local 16384 in bf16, at M_local 16384 in fp16 with the
+    pages' 256x256 output tile, and at M_local 16384 in fp16 with B stored N-contiguous (a row-major K x N
+    matrix), W=8, timed like the headline."""
     import torch
     from gemm_all_gather_amd import binding as ag
 
     res = {}
     region = views[0].geometry().bytes_per_rank
-    for name, M, dtype, layout in (("M1024_f16", 1024, "f16", "k"), ("M16384_bf16", 16384, "bf16", "k"),
-                                   ("M16384_f16_B_row_major_KxN", 16384, "f16", "n")):
+    for name, M, dtype, layout, tile in (("M1024_f16", 1024, "f16", "k", (0, 0, 0)),
+                                         ("M16384_bf16", 16384, "bf16", "k", (0, 0, 0)),
+                                         ("M16384_f16_tile_256x256x64", 16384, "f16", "k", (256, 256, 64)),
+                                         ("M16384_f16_B_row_major_KxN", 16384, "f16", "n", (0, 0, 0))):
         sub = argparse.Namespace(**vars(args))
         if M * FU_N * FU_K < (1 << 36):
             # short calls (~75 us): the headline's warm-up steps, so the clocks settle after the workloads
@@ -345,7 +361,7 @@ def _context_fused(args, stream, timed, views, fu_off):
         fb = _device_normal(FU_N * FU_K, dtype, FU_K ** -0.5, 1300)    # the N x K (or K x N) B: same count
         ldb = FU_K if layout == "k" else FU_N
         ms, _ = timed(lambda: [ag.gemm_all_gather_ex(vws[j], FU_W, 0, 1, fa[j], FU_K, fb, ldb, off, M, FU_N,
-                                                     FU_K, dtype, 0, 0, 0, 0, b_layout=layout, stream=stream)
+                                                     FU_K, dtype, *tile, 0, b_layout=layout, stream=stream)
                                for j in range(FU_W)], sub)
         flops = 2.0 * M * FU_N * FU_K
         tf = FU_W * flops / (ms / 1e3) / 1e12
@@ -532,13 +548,16 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(per_call_bytes / copy_launch_s / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": _traffic(f"ag_copy_kernel_w8_{AG_M}x{AG_N}_f16_pmc.md", "ag_copy.hip", per_call_bytes),
-            "kernel": f"ag_copy_kernel<VEC={ag_plan.vec_bytes},W={AG_W},VPT={ag_plan.vectors_per_thread}>",
+            "kernel": (f"ag_copy_ticket_kernel<VEC={ag_plan.vec_bytes},W={AG_W},VPT={ag_plan.vectors_per_thread},"
+                       f"G={ag_plan.tiles_per_ticket}>" if ag_plan.tile_order == ag.AG_ORDER_TICKETS else
+                       f"ag_copy_kernel<VEC={ag_plan.vec_bytes},W={AG_W},VPT={ag_plan.vectors_per_thread}>"),
             "alg_bytes_per_launch": per_call_bytes,
             "avg_launch_us": round(copy_launch_s * 1e6, 3),
         }
         out["spread"] = spread.get(id(copy_job))
         out["plan_all_gather"] = {k: ag_plan.as_dict()[k] for k in ("vec_bytes", "n_programs", "threads",
-                                                                    "total_tiles", "vectors_per_thread")}
+                                                                    "total_tiles", "vectors_per_thread",
+                                                                    "tile_order", "tiles_per_ticket")}
         out["copy_ms_per_job"] = round(copy_ms, 5)
     if fused_ok:
         flops = fu_plan.flops

@@ -48,7 +48,8 @@ class Plan(ctypes.Structure):
                 ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("total_tiles", ctypes.c_int64),
                 ("rank_block_offset", ctypes.c_uint64), ("bytes_read", ctypes.c_uint64),
                 ("bytes_written", ctypes.c_uint64), ("flops", ctypes.c_double),
-                ("dest_group", ctypes.c_int32), ("schedule", ctypes.c_int32)]
+                ("dest_group", ctypes.c_int32), ("schedule", ctypes.c_int32),
+                ("tile_order", ctypes.c_int32), ("tiles_per_ticket", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -56,23 +57,26 @@ class Plan(ctypes.Structure):
 
 AG_SCHEDULE_TILES, AG_SCHEDULE_PARTITIONED = 0, 1
 SCHEDULES = {"tiles": AG_SCHEDULE_TILES, "partitioned": AG_SCHEDULE_PARTITIONED}
+AG_ORDER_AUTO, AG_ORDER_STRIDE, AG_ORDER_TICKETS = 0, 1, 2
+TILE_ORDERS = {"auto": AG_ORDER_AUTO, "stride": AG_ORDER_STRIDE, "tickets": AG_ORDER_TICKETS}
 AG_B_K_CONTIGUOUS, AG_B_N_CONTIGUOUS = 0, 1
 B_LAYOUTS = {"k": AG_B_K_CONTIGUOUS, "n": AG_B_N_CONTIGUOUS}
 
 
 class CopyOptions(ctypes.Structure):
-    _fields_ = [("dest_group", ctypes.c_int32), ("schedule", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+    _fields_ = [("dest_group", ctypes.c_int32), ("schedule", ctypes.c_int32), ("tile_order", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 5)]
 
 
 class GemmOptions(ctypes.Structure):
     _fields_ = [("b_layout", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
 
 
-def _options(dest_group=0, schedule=0) -> CopyOptions:
+def _options(dest_group=0, schedule=0, tile_order=0) -> CopyOptions:
     o = CopyOptions()
     o.dest_group = dest_group
     o.schedule = SCHEDULES[schedule] if isinstance(schedule, str) else schedule
+    o.tile_order = TILE_ORDERS[tile_order] if isinstance(tile_order, str) else tile_order
     return o
 
 
@@ -270,9 +274,9 @@ def all_gather(heap: Heap, W, rank_start, rank_stride, input, out_offset, M_loca
 
 
 def plan_all_gather_ex(geom: Geometry, W, rank_start, rank_stride, input_addr, out_offset, M_local, N, dtype,
-                       tile_m=0, tile_n=0, n_programs=0, dest_group=0, schedule=0) -> Plan:
+                       tile_m=0, tile_n=0, n_programs=0, dest_group=0, schedule=0, tile_order=0) -> Plan:
     p = Plan()
-    o = _options(dest_group, schedule)
+    o = _options(dest_group, schedule, tile_order)
     _check(lib().ag_plan_all_gather_ex(ctypes.byref(geom), W, rank_start, rank_stride, _ptr(input_addr), out_offset,
                                        M_local, N, _dtype(dtype), tile_m, tile_n, n_programs, ctypes.byref(o),
                                        ctypes.byref(p)), "ag_plan_all_gather_ex")
@@ -280,8 +284,8 @@ def plan_all_gather_ex(geom: Geometry, W, rank_start, rank_stride, input_addr, o
 
 
 def all_gather_ex(heap: Heap, W, rank_start, rank_stride, input, out_offset, M_local, N, dtype,
-                  tile_m=0, tile_n=0, n_programs=0, dest_group=0, schedule=0, stream=None) -> None:
-    o = _options(dest_group, schedule)
+                  tile_m=0, tile_n=0, n_programs=0, dest_group=0, schedule=0, stream=None, tile_order=0) -> None:
+    o = _options(dest_group, schedule, tile_order)
     _check(lib().ag_all_gather_ex(heap.handle, W, rank_start, rank_stride, _ptr(input), out_offset, M_local, N,
                                   _dtype(dtype), tile_m, tile_n, n_programs, ctypes.byref(o), _stream(stream)),
            "ag_all_gather_ex")
@@ -303,9 +307,9 @@ def all_to_all(heap: Heap, W, rank_start, rank_stride, input, out_offset, M_chun
 
 
 def plan_all_to_all_ex(geom: Geometry, W, rank_start, rank_stride, input_addr, out_offset, M_chunk, N, dtype,
-                       tile_m=0, tile_n=0, n_programs=0, dest_group=0, schedule=0) -> Plan:
+                       tile_m=0, tile_n=0, n_programs=0, dest_group=0, schedule=0, tile_order=0) -> Plan:
     p = Plan()
-    o = _options(dest_group, schedule)
+    o = _options(dest_group, schedule, tile_order)
     _check(lib().ag_plan_all_to_all_ex(ctypes.byref(geom), W, rank_start, rank_stride, _ptr(input_addr), out_offset,
                                        M_chunk, N, _dtype(dtype), tile_m, tile_n, n_programs, ctypes.byref(o),
                                        ctypes.byref(p)), "ag_plan_all_to_all_ex")
@@ -313,8 +317,8 @@ def plan_all_to_all_ex(geom: Geometry, W, rank_start, rank_stride, input_addr, o
 
 
 def all_to_all_ex(heap: Heap, W, rank_start, rank_stride, input, out_offset, M_chunk, N, dtype,
-                  tile_m=0, tile_n=0, n_programs=0, dest_group=0, schedule=0, stream=None) -> None:
-    o = _options(dest_group, schedule)
+                  tile_m=0, tile_n=0, n_programs=0, dest_group=0, schedule=0, stream=None, tile_order=0) -> None:
+    o = _options(dest_group, schedule, tile_order)
     _check(lib().ag_all_to_all_ex(heap.handle, W, rank_start, rank_stride, _ptr(input), out_offset, M_chunk, N,
                                   _dtype(dtype), tile_m, tile_n, n_programs, ctypes.byref(o), _stream(stream)),
            "ag_all_to_all_ex")

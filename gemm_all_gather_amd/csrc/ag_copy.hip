@@ -288,6 +288,172 @@ __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
     }
 }
 
+// Ticket order.  The same persistent programs and the same per-tile work (each
+// tile loaded once, then stored to the local region and the rotated peers),
+// but the programs take their tiles from a device counter in increasing
+// order, G consecutive tiles per ticket, instead of walking a fixed grid
+// stride.  Programs of a grid stride drift apart, so over a long call the
+// tiles in flight spread over an ever wider address range of the W+1
+// streams; tickets keep them in one compact window, as the hardware
+// dispatcher does for a grid of one workgroup per tile, and the HBM streams
+// stay dense (W=8, 16384x8192 fp16, 256 programs: 373 against 448 us per call
+// in a measured replica).  Each ticket is one relaxed device-scope atomic
+// add, taken by one thread and handed to the workgroup through LDS; it is
+// taken before the stores of the batch in hand, so waiting for it never waits
+// for those stores.  The last program to finish resets the counter, so it is
+// zero at every launch.  Two batches of G tiles live in registers: the next
+// one loading while the one in hand is stored.
+template <int VEC, int W, int VPT, int G, bool WIDE>
+__global__ __launch_bounds__(256) void ag_copy_ticket_kernel(CopyKernelArgs a)
+{
+    constexpr int kAux = WIDE ? AG_COPY_STORE_AUX_WIDE : AG_COPY_STORE_AUX;
+    using VT = Vec<VEC>;
+    using V = typename VT::T;
+    __shared__ uint32_t s_ticket[2];
+
+    const uint64_t input = reinterpret_cast<uint64_t>(a.input);
+    const uint64_t block_bytes = static_cast<uint64_t>(a.rows) * a.row_bytes;
+    uint32_t* const counter = a.tickets;
+
+    const uint32_t lane = threadIdx.x;
+    const uint32_t vpr_mask = (1u << a.vecs_per_row_log2) - 1u;
+    uint32_t lane_off[VPT], lane_col[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const uint32_t idx = lane + 256u * j;
+        lane_col[j] = (idx & vpr_mask) * VEC;
+        lane_off[j] = (idx >> a.vecs_per_row_log2) * static_cast<uint32_t>(a.row_bytes) + lane_col[j];
+    }
+    // tile -> byte origin and extent; tiles past the last one get no records (every access dropped)
+    auto origin = [&](uint32_t tile) {
+        TileRef r;
+        const bool valid = tile < a.total_tiles;
+        const uint32_t tt = valid ? tile : 0u;
+        const uint32_t tm = tt / a.tiles_n;
+        const uint32_t tn = tt - tm * a.tiles_n;
+        r.col0 = tn * a.tile_row_bytes;
+        r.off = static_cast<uint64_t>(tm) * a.tile_m * a.row_bytes + r.col0;
+        const uint64_t left = valid ? block_bytes - r.off : 0;
+        r.records = static_cast<uint32_t>(left < 0x7fffffffull ? left : 0x7fffffffull);
+        r.full = r.col0 + a.tile_row_bytes <= a.row_bytes;
+        return r;
+    };
+    auto load_batch = [&](uint32_t first, V (&v)[G][VPT]) {
+#pragma unroll
+        for (int b = 0; b < G; ++b) {
+            const TileRef r = origin(first + b);
+            const __amdgpu_buffer_rsrc_t src = make_rsrc(input + r.off, r.records);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j)
+                v[b][j] = VT::load(src, (r.full || r.col0 + lane_col[j] < a.row_bytes) ? lane_off[j] : kOutOfRange);
+        }
+    };
+    // The next ticket: G tiles from the counter, which counts tickets (lane 0 of wave 0; the others
+    // get it through LDS).  An increment (atomic inc with no wrap point), not an add: the compiler
+    // rewrites a lone add into a wave-wide add whose result it distributes to the lanes at once, which
+    // would wait for the atomic right where it is issued, before the stores that follow it.
+    // The ticket number goes through LDS as it comes back (nothing is computed from it in lane 0),
+    // and the first tile of the ticket is G times the number.
+    auto take = [&]() -> uint32_t {
+        return __builtin_amdgcn_atomic_inc32(counter, 0xffffffffu, __ATOMIC_RELAXED, "agent");
+    };
+    auto share = [&](uint32_t ticket, int slot) -> uint32_t {
+        if (threadIdx.x == 0) s_ticket[slot] = ticket;
+        __syncthreads();
+        return s_ticket[slot] * static_cast<uint32_t>(G);
+    };
+
+    // ---- destinations, once, before the tile loop: one vector load of the table (lane i:
+    // destination i = member (g + i) mod W, lane W: the local base), then readlane
+    uint64_t table_entry;
+    {
+        const int l = static_cast<int>(threadIdx.x & 63u);
+        int entry = a.rank;
+        if (l < W) {
+            int gi = a.group_rank + l;
+            if (gi >= W) gi -= W;
+            entry = a.rank_start + gi * a.rank_stride;
+        }
+        table_entry = a.heap_bases[entry];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // the table load goes out first
+
+    uint32_t first = share(threadIdx.x == 0 ? take() : 0u, 0);
+    int slot = 1;
+    V va[G][VPT], vb[G][VPT];
+    uint32_t ta = first, tb = 0;
+    bool live = ta < a.total_tiles;
+    if (live) {
+        load_batch(ta, va);
+        tb = share(threadIdx.x == 0 ? take() : 0u, slot);
+        slot ^= 1;
+        load_batch(tb, vb);
+
+        uint64_t dest[W];
+        {
+            const uint32_t lo = static_cast<uint32_t>(table_entry), hi = static_cast<uint32_t>(table_entry >> 32);
+            const uint64_t local_base = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(hi, W))) << 32) |
+                                        static_cast<uint32_t>(__builtin_amdgcn_readlane(lo, W));
+            const uint64_t out_local = local_base + a.rank_block_offset;
+#pragma unroll
+            for (int i = 0; i < W; ++i) {
+                const uint64_t b = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(hi, i))) << 32) |
+                                   static_cast<uint32_t>(__builtin_amdgcn_readlane(lo, i));
+                dest[i] = out_local + static_cast<uint64_t>(static_cast<int64_t>(b - local_base));
+            }
+        }
+        auto store_batch = [&](uint32_t first_tile, const V (&v)[G][VPT]) {
+#pragma unroll
+            for (int b = 0; b < G; ++b) {
+                const TileRef r = origin(first_tile + b);
+#pragma unroll
+                for (int i = 0; i < W; ++i) {   // local region first, then the rotated peers
+                    const __amdgpu_buffer_rsrc_t dst = make_rsrc(dest[i] + r.off, r.records);
+#pragma unroll
+                    for (int j = 0; j < VPT; ++j)
+                        VT::template store<kAux>(v[b][j], dst,
+                                                 (r.full || r.col0 + lane_col[j] < a.row_bytes) ? lane_off[j] : kOutOfRange);
+                }
+            }
+        };
+        // Invariant: va holds batch ta (in hand, ta < total), vb batch tb (loading); tickets rise.
+        // The ticket is defined only in lane 0 and used only there: no value is merged in for the
+        // other lanes, so nothing overwrites its register while the atomic is in flight and its
+        // wait (at the LDS write, after the stores) covers only what was issued before it.
+        auto post = [&](uint32_t tk, int sl) -> uint32_t {
+            if (threadIdx.x == 0) s_ticket[sl] = tk;
+            __syncthreads();
+            return s_ticket[sl] * static_cast<uint32_t>(G);
+        };
+        for (;;) {
+            bool more = tb < a.total_tiles;
+            uint32_t tk;
+            if (more && threadIdx.x == 0) tk = take();   // the batch after tb, before ta's stores
+            store_batch(ta, va);
+            if (!more) break;
+            ta = post(tk, slot);
+            slot ^= 1;
+            load_batch(ta, va);
+
+            more = ta < a.total_tiles;
+            if (more && threadIdx.x == 0) tk = take();
+            store_batch(tb, vb);
+            if (!more) break;
+            tb = post(tk, slot);
+            slot ^= 1;
+            load_batch(tb, vb);
+        }
+    }
+    // the last program to finish puts the counter back to zero for the next launch
+    if (threadIdx.x == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(counter + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done + 1 == gridDim.x) {
+            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(counter + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 // All-to-all: tile t of every input chunk is loaded (chunk (g + i) mod W
 // for destination i), then tile t of destination i's block receives it,
 // local region first, then the rotated peers.  The W chunk tiles of the next
@@ -498,6 +664,48 @@ CopyFn pick_a2a_world(int w, int vpt, bool wide)
     }
 }
 
+// ---- ticket-order all-gather instantiations: 16-byte vectors, W = 1..8, one or two vectors per
+// thread per tile, 4, 8 or 16 tiles per ticket
+template <int W, int VPT>
+CopyFn pick_ticket_g(int ticket, bool wide)
+{
+    switch (ticket) {
+    case 4: return wide ? ag_copy_ticket_kernel<16, W, VPT, 4, true> : ag_copy_ticket_kernel<16, W, VPT, 4, false>;
+    case 8: return wide ? ag_copy_ticket_kernel<16, W, VPT, 8, true> : ag_copy_ticket_kernel<16, W, VPT, 8, false>;
+    case 16:
+        if constexpr (VPT == 1)
+            return wide ? ag_copy_ticket_kernel<16, W, VPT, 16, true> : ag_copy_ticket_kernel<16, W, VPT, 16, false>;
+        return nullptr;
+    default: return nullptr;
+    }
+}
+
+template <int W>
+CopyFn pick_ticket_vpt(int vpt, int ticket, bool wide)
+{
+    switch (vpt) {
+    case 1: return pick_ticket_g<W, 1>(ticket, wide);
+    case 2: return ticket <= 8 ? pick_ticket_g<W, 2>(ticket, wide) : nullptr;   // at most 16 vectors per batch
+    default: return nullptr;
+    }
+}
+
+CopyFn pick_ticket(int vec, int w, int vpt, int ticket, bool wide)
+{
+    if (vec != 16) return nullptr;
+    switch (w) {
+    case 1: return pick_ticket_vpt<1>(vpt, ticket, wide);
+    case 2: return pick_ticket_vpt<2>(vpt, ticket, wide);
+    case 3: return pick_ticket_vpt<3>(vpt, ticket, wide);
+    case 4: return pick_ticket_vpt<4>(vpt, ticket, wide);
+    case 5: return pick_ticket_vpt<5>(vpt, ticket, wide);
+    case 6: return pick_ticket_vpt<6>(vpt, ticket, wide);
+    case 7: return pick_ticket_vpt<7>(vpt, ticket, wide);
+    case 8: return pick_ticket_vpt<8>(vpt, ticket, wide);
+    default: return nullptr;
+    }
+}
+
 CopyFn pick_kernel(int kind, int vec, int w, int g, int vpt, bool part, bool wide)
 {
     // the partitioned all-to-all runs the partitioned copy kernel (one destination per program)
@@ -527,8 +735,21 @@ bool copy_supported(int kind, int vec_bytes, int dests, int group, int vpt, bool
     return pick_kernel(kind, vec_bytes, dests, group, vpt, partitioned, false) != nullptr;
 }
 
+bool copy_ticket_supported(int vec_bytes, int dests, int vpt, int ticket)
+{
+    return pick_ticket(vec_bytes, dests, vpt, ticket, false) != nullptr;
+}
+
 hipError_t launch_copy(const CopyLaunch& l, hipStream_t stream)
 {
+    if (l.ticket != 0) {
+        CopyFn fn = l.kind == kCopyAllGather && l.group == 0 && !l.args.partitioned && l.args.slices == 1
+                        ? pick_ticket(l.vec_bytes, l.dests, l.vpt, l.ticket, l.wide != 0)
+                        : nullptr;
+        if (fn == nullptr || l.grid < 1 || l.args.tickets == nullptr) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(fn, dim3(l.grid), dim3(256), 0, stream, l.args);
+        return hipGetLastError();
+    }
     CopyFn fn = pick_kernel(l.kind, l.vec_bytes, l.dests, l.group, l.vpt, l.args.partitioned != 0, l.wide != 0);
     const uint32_t max_slices = l.kind == kCopyAllToAll ? 1 : 4;
     if (fn == nullptr || l.args.slices < 1 || l.args.slices > max_slices || l.grid < 1 || l.args.world < 1)

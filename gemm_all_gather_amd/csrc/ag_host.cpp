@@ -74,9 +74,14 @@ bool overlaps(uint64_t a0, uint64_t an, uint64_t b0, uint64_t bn)
     return an != 0 && bn != 0 && a0 < b0 + bn && b0 < a0 + an;
 }
 
+// Bytes of device memory per rank for its tile counter (ticket order): two uint32 words used, one
+// 64-byte block per rank so that no two ranks' counters share a line.
+constexpr uint64_t kTicketBytes = 64;
+
 struct HeapCore {
     void* slab = nullptr;
-    uint64_t* table = nullptr;  // device uint64_t[n_ranks]
+    uint64_t* table = nullptr;  // device uint64_t[n_ranks], followed (256-byte aligned) by the tile counters
+    uint32_t* tickets = nullptr;  // device, kTicketBytes per rank; zero between calls
     int n_ranks = 0;
     uint64_t bytes_per_rank = 0;
     bool owns_slab = false;
@@ -108,16 +113,20 @@ ag_status_t finish_heap(std::shared_ptr<HeapCore> core, ag_heap_t** out)
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
     e = hipDeviceGetAttribute(&core->num_cus, hipDeviceAttributeMultiprocessorCount, core->device);
     if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(multiProcessorCount)");
-    std::vector<uint64_t> bases(core->n_ranks);
+    // one device allocation: the base table, then (256-byte aligned) one zeroed tile counter per rank
+    const uint64_t table_bytes = ceil_div(sizeof(uint64_t) * core->n_ranks, 256) * 256;
+    const uint64_t total = table_bytes + kTicketBytes * core->n_ranks;
+    std::vector<uint64_t> host(total / sizeof(uint64_t), 0);
     for (int r = 0; r < core->n_ranks; ++r)
-        bases[r] = reinterpret_cast<uint64_t>(core->slab) + static_cast<uint64_t>(r) * core->bytes_per_rank;
-    e = hipMalloc(reinterpret_cast<void**>(&core->table), sizeof(uint64_t) * core->n_ranks);
+        host[r] = reinterpret_cast<uint64_t>(core->slab) + static_cast<uint64_t>(r) * core->bytes_per_rank;
+    e = hipMalloc(reinterpret_cast<void**>(&core->table), total);
     if (e != hipSuccess) {
         core->table = nullptr;
         return fail_hip(e, "hipMalloc(heap_bases)");
     }
-    e = hipMemcpy(core->table, bases.data(), sizeof(uint64_t) * core->n_ranks, hipMemcpyHostToDevice);
+    e = hipMemcpy(core->table, host.data(), total, hipMemcpyHostToDevice);
     if (e != hipSuccess) return fail_hip(e, "hipMemcpy(heap_bases)");
+    core->tickets = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(core->table) + table_bytes);
     auto* h = new (std::nothrow) ag_heap;
     if (!h) return fail(AG_ERR_OUT_OF_MEMORY, "host allocation of the heap handle failed");
     h->core = std::move(core);
@@ -414,10 +423,14 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     const char* mname = a2a ? "M_chunk" : "M_local";
     ag_copy_options_t opt{};
     if (options) opt = *options;
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < 5; ++i)
         if (opt.reserved[i] != 0) return fail(AG_ERR_INVALID_ARG, "options->reserved[%d] is not 0", i);
     if (opt.schedule != AG_SCHEDULE_TILES && opt.schedule != AG_SCHEDULE_PARTITIONED)
         return fail(AG_ERR_INVALID_ARG, "unknown schedule %d", opt.schedule);
+    if (opt.tile_order != AG_ORDER_AUTO && opt.tile_order != AG_ORDER_STRIDE && opt.tile_order != AG_ORDER_TICKETS)
+        return fail(AG_ERR_INVALID_ARG, "unknown tile_order %d", opt.tile_order);
+    if (opt.tile_order != AG_ORDER_AUTO && (a2a || opt.schedule != AG_SCHEDULE_TILES))
+        return fail(AG_ERR_INVALID_ARG, "tile_order applies to the all-gather's tile schedule only");
     if (opt.dest_group < 0) return fail(AG_ERR_INVALID_ARG, "dest_group %d < 0", opt.dest_group);
     if (opt.dest_group != 0 && opt.dest_group != 1 && opt.dest_group != 2 && opt.dest_group != 4)
         return fail(AG_ERR_UNSUPPORTED, "dest_group %d: 0, 1, 2 or 4 are supported", opt.dest_group);
@@ -525,8 +538,29 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     if (total >= (uint64_t{1} << 31)) return fail(AG_ERR_UNSUPPORTED, "more than 2^31 tiles");
 
     const uint64_t programs = n_programs == 0 ? geom->num_cus : n_programs;
+    // Tile order of the tile schedule.  Tickets (consecutive tiles handed out in increasing order
+    // from the rank's counter) keep the tiles in flight in one compact window; they pay a counter
+    // round trip per ticket, which long calls hide and short ones do not (at 1024x4096 fp16, W=8,
+    // 16 tiles per program: 15.9 against 11.8 us per call).
+    int ticket = 0;
+    {
+        const int tvpt = static_cast<int>(tile_vecs / 256);
+        int g = programs >= 256 ? 4 : programs >= 128 ? 8 : 16;
+        if (tvpt == 2 && g > 8) g = 8;
+        const bool fits = !part && !a2a && p.dest_group == 0 && ag::copy_ticket_supported(vec, W, tvpt, g);
+        if (opt.tile_order == AG_ORDER_TICKETS) {
+            if (!fits)
+                return fail(AG_ERR_UNSUPPORTED, "no ticket-order kernel for this call (%d-byte vectors, %d per thread, "
+                            "destination group %d)", vec, tvpt, p.dest_group);
+            ticket = g;
+        } else if (opt.tile_order == AG_ORDER_AUTO && fits && total >= 64 * programs) {
+            ticket = g;
+        }
+    }
     uint64_t slices = 1, grid = 0;
-    if (part) {
+    if (ticket) {
+        grid = std::min<uint64_t>(programs, ceil_div(total, static_cast<uint64_t>(ticket)));
+    } else if (part) {
         // W equal sets of programs, one per destination, each walking all tiles
         const uint64_t per_dest = std::min<uint64_t>(std::max<uint64_t>(programs / W, 1), total);
         grid = per_dest * W;
@@ -551,6 +585,8 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     p.n_programs = static_cast<int32_t>(grid);
     p.threads = static_cast<int32_t>(256 * slices);
     p.variant = kind;
+    p.tile_order = ticket ? AG_ORDER_TICKETS : AG_ORDER_STRIDE;
+    p.tiles_per_ticket = ticket;
     *plan = p;
     return ok();
 }
@@ -604,6 +640,11 @@ ag_status_t launch_copy_call(const ag_heap_t* heap, int kind, int W, int rank_st
     l.grid = p.n_programs;
     // streaming stores with system scope on wide launches whose stores are never waited for
     l.wide = (p.dest_group == 0 && 2 * static_cast<int64_t>(p.n_programs) >= geom.num_cus) ? 1 : 0;
+    // ticket order: the calling rank's counter (zero between calls; calls of one rank never overlap)
+    l.ticket = p.tiles_per_ticket;
+    l.args.tickets = p.tiles_per_ticket
+                         ? heap->core->tickets + (kTicketBytes / sizeof(uint32_t)) * static_cast<uint64_t>(geom.rank)
+                         : nullptr;
     const hipError_t e2 = ag::launch_copy(l, static_cast<hipStream_t>(stream));
     if (e2 != hipSuccess) return fail_hip(e2, kind == ag::kCopyAllToAll ? "all-to-all kernel launch" : "all-gather kernel launch");
     return ok();

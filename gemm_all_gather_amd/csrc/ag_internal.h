@@ -28,6 +28,8 @@ struct CopyKernelArgs {
     uint32_t world;               // group size W
     uint32_t partitioned;         // 1: program p stores only to destination p % W (the partitioned kernel)
     uint32_t reserved;
+    uint32_t* tickets;            // ticket order: device uint32_t[2] = {next tile, programs finished}, zero at
+                                  // launch; the last program to finish sets both back to zero (else unused)
 };
 
 enum CopyKind { kCopyAllGather = 0, kCopyAllToAll = 1 };
@@ -41,10 +43,13 @@ struct CopyLaunch {
     int vpt;           // vector accesses per thread per tile
     int grid;          // workgroups
     int wide;          // 1: the store policy of launches on at least half the CUs (no destination groups)
+    int ticket;        // tiles per ticket of the ticket order (0: grid-stride order)
 };
 
 // Whether the launcher has a kernel for (kind, vec, dests, group, vpt, schedule) (host-only).
 bool copy_supported(int kind, int vec_bytes, int dests, int group, int vpt, bool partitioned);
+// Whether the ticket-order all-gather kernel exists for (vec, dests, vpt, tiles per ticket) (host-only).
+bool copy_ticket_supported(int vec_bytes, int dests, int vpt, int ticket);
 hipError_t launch_copy(const CopyLaunch& l, hipStream_t stream);
 
 // Arguments of the fused GEMM + multi-destination store kernel.

@@ -94,6 +94,8 @@ typedef struct ag_plan {
     double flops;                /* 2*M_local*N*K for the GEMM, 0 for the all-gather */
     int32_t dest_group;          /* copy kernels: destinations stored per wait (0 = all of them, no wait) */
     int32_t schedule;            /* copy kernels: ag_schedule_t of the launch */
+    int32_t tile_order;          /* copy kernels: ag_tile_order_t applied (AG_ORDER_STRIDE or AG_ORDER_TICKETS) */
+    int32_t tiles_per_ticket;    /* copy kernels with AG_ORDER_TICKETS: consecutive tiles per ticket (else 0) */
 } ag_plan_t;
 
 /* Tile schedules of the all-gather (ag_all_gather_ex) and the all-to-all (ag_all_to_all_ex). */
@@ -102,13 +104,26 @@ typedef enum ag_schedule {
     AG_SCHEDULE_PARTITIONED = 1  /* each program owns one destination and walks the tiles for it alone */
 } ag_schedule_t;
 
+/* Order in which the persistent programs of AG_SCHEDULE_TILES take their tiles.  The result does
+ * not depend on it. */
+typedef enum ag_tile_order {
+    AG_ORDER_AUTO = 0,     /* the library's choice: AG_ORDER_TICKETS for calls of at least 64 tiles per
+                              program where a ticket kernel exists, AG_ORDER_STRIDE otherwise */
+    AG_ORDER_STRIDE = 1,   /* fixed grid stride: program p takes tiles p, p + P, p + 2P, ... */
+    AG_ORDER_TICKETS = 2   /* programs take G consecutive tiles at a time from a device counter of the
+                              calling rank, in increasing tile order (G = 4 at 256 or more programs, 8 at
+                              128 or more, 16 below; 8 at most for two vectors per thread); 16-byte
+                              vectors, one or two per thread and tile, no destination groups */
+} ag_tile_order_t;
+
 /* Options of ag_all_gather_ex and ag_all_to_all_ex; all-zero (or a NULL pointer) is the plain call. */
 typedef struct ag_copy_options {
     int32_t dest_group;   /* 0: one straight run of W destination stores per tile (default).
                              1, 2 or 4 (< W): store that many destinations, then wait until the
                              stores before them have completed, then the next group */
     int32_t schedule;     /* ag_schedule_t */
-    int32_t reserved[6];  /* must be 0 */
+    int32_t tile_order;   /* ag_tile_order_t (all-gather with AG_SCHEDULE_TILES only; else 0) */
+    int32_t reserved[5];  /* must be 0 */
 } ag_copy_options_t;
 
 /* ------------------------------------------------------------------------
@@ -208,9 +223,13 @@ ag_status_t ag_heap_info(const ag_heap_t* heap, int* n_ranks, int* rank, size_t*
  * changes.  The input tile is read once and stored to the local region
  * first, then to the peers in rotated group order (g+1, g+2, ... mod W).
  * Calls for different ranks of a group write disjoint rows and may run
- * concurrently on different streams.  M_local = 0 is a no-op.  input must
- * not overlap any member's output block, except that it may be exactly this
- * rank's own rows in its own region (in-place).
+ * concurrently on different streams.  Calls for the same rank must not
+ * overlap in time (order them on one stream): a call in ticket order
+ * (AG_ORDER_TICKETS, the library's choice for long calls) takes its tiles
+ * from a counter the heap keeps for each rank, zero between calls.
+ * M_local = 0 is a no-op.  input must not overlap any member's output
+ * block, except that it may be exactly this rank's own rows in its own
+ * region (in-place).
  * ------------------------------------------------------------------------ */
 ag_status_t ag_all_gather(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
                           const void* input, size_t out_offset, int64_t M_local, int64_t N,
@@ -244,8 +263,17 @@ ag_status_t ag_plan_all_gather(const ag_heap_geometry_t* geom, int W, int rank_s
  *               tile is read W times (once per destination).  n_programs is
  *               rounded down to a multiple of W (at least W); dest_group
  *               must be 0.
- * Plan: ag_plan_all_gather_ex reports dest_group and schedule as applied
- * and bytes_read of the schedule (W times the input when partitioned).
+ * options->tile_order  ag_tile_order_t, for AG_SCHEDULE_TILES without
+ *               destination groups: AG_ORDER_STRIDE or AG_ORDER_TICKETS force
+ *               the order (AG_ERR_UNSUPPORTED where no ticket kernel fits the
+ *               call: vectors other than 16 bytes or more than two per thread,
+ *               destination groups, the partitioned schedule).  Ticket order
+ *               at 256 programs, W=8, 16384x8192 fp16: 6.4 TB/s against 5.3
+ *               for the grid stride; below about 64 tiles per program the
+ *               counter's round trips cost more than they save.
+ * Plan: ag_plan_all_gather_ex reports dest_group, schedule and tile_order as
+ * applied, and bytes_read of the schedule (W times the input when
+ * partitioned).
  * ------------------------------------------------------------------------ */
 ag_status_t ag_all_gather_ex(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
                              const void* input, size_t out_offset, int64_t M_local, int64_t N,
@@ -287,7 +315,8 @@ ag_status_t ag_plan_all_to_all(const ag_heap_geometry_t* geom, int W, int rank_s
                                ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, ag_plan_t* plan);
 
 /* ag_all_to_all with options (NULL or all-zero = ag_all_to_all).  Same
- * result.  dest_group must be 0 (AG_ERR_INVALID_ARG otherwise).  schedule
+ * result.  dest_group and tile_order must be 0 (AG_ERR_INVALID_ARG
+ * otherwise).  schedule
  * AG_SCHEDULE_PARTITIONED (the partitioned schedule of ag_all_gather_ex
  * applied to the exchange): program p owns destination i = p mod W of the
  * rotated order and copies chunk (g + i) mod W there, the programs of one

@@ -452,3 +452,71 @@ def test_gemm_plan_n_contiguous_b_extent_is_k_rows():
     b_bytes = ((8192 - 1) * 3584 + 3584) * 2
     assert status_of(gplan_ex, g=g, b=SLAB - b_bytes)[0] == ag.AG_OK
     assert status_of(gplan_ex, g=g, b=SLAB - b_bytes + 16)[0] == ag.AG_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# tile order of the all-gather's tile schedule: grid stride or tickets
+# ---------------------------------------------------------------------------
+
+BIG = dict(M=16384, N=8192)
+
+
+def _big_geom(e=2, **kw):
+    return geom(bytes_per_rank=8 * 16384 * 8192 * e + MiB, **kw)
+
+
+@pytest.mark.parametrize("progs,ticket", [(256, 4), (0, 4), (128, 8), (64, 16)])
+def test_plan_tickets_for_long_calls(progs, ticket):
+    p = plan(g=_big_geom(), progs=progs, **BIG)
+    assert p.tile_order == ag.AG_ORDER_TICKETS and p.tiles_per_ticket == ticket
+    assert p.threads == 256 and p.n_programs == (progs or 256)
+    assert p.total_tiles == 2048 * 32 and p.vectors_per_thread == 1
+
+
+def test_plan_tickets_two_vectors_per_thread_at_most_eight():
+    p = plan(g=_big_geom(e=4), dtype="f32", progs=64, **BIG)       # 8x256 fp32: two 16-byte vectors
+    assert p.vectors_per_thread == 2 and p.tile_order == ag.AG_ORDER_TICKETS and p.tiles_per_ticket == 8
+    p = plan(g=_big_geom(), tm=16, tn=512, progs=256, **BIG)        # four vectors per thread: no ticket kernel
+    assert p.vectors_per_thread == 4 and p.tile_order == ag.AG_ORDER_STRIDE and p.tiles_per_ticket == 0
+
+
+def test_plan_short_calls_keep_the_grid_stride():
+    p = plan(progs=128)                                            # 1024x4096: 16 tiles per program
+    assert p.tile_order == ag.AG_ORDER_STRIDE and p.tiles_per_ticket == 0
+    p = ag.plan_all_gather_ex(geom(), 8, 0, 1, INPUT, 0, 1024, 4096, "f16", 0, 0, 128, tile_order="tickets")
+    assert p.tile_order == ag.AG_ORDER_TICKETS and p.tiles_per_ticket == 8 and p.n_programs == 128
+    p = ag.plan_all_gather_ex(_big_geom(), 8, 0, 1, INPUT, 0, 16384, 8192, "f16", 0, 0, 64, tile_order="stride")
+    assert p.tile_order == ag.AG_ORDER_STRIDE and p.threads == 1024      # narrow launch: four slices
+
+
+def test_plan_ticket_grid_is_capped_by_tickets():
+    p = ag.plan_all_gather_ex(geom(), 8, 0, 1, INPUT, 0, 64, 256, "f16", 8, 256, 256, tile_order="tickets")
+    assert p.total_tiles == 8 and p.tiles_per_ticket == 4 and p.n_programs == 2
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tile_order="tickets", dest_group=2), ag.AG_ERR_UNSUPPORTED),
+    (dict(tile_order="tickets", schedule="partitioned"), ag.AG_ERR_INVALID_ARG),
+    (dict(tile_order="stride", schedule="partitioned"), ag.AG_ERR_INVALID_ARG),
+    (dict(tile_order=3), ag.AG_ERR_INVALID_ARG),
+])
+def test_plan_tile_order_rejects(kw, status):
+    got, _ = status_of(ag.plan_all_gather_ex, geom(), 8, 0, 1, INPUT, 0, 1024, 4096, "f16", 0, 0, 0, **kw)
+    assert got == status
+
+
+def test_plan_tickets_need_16_byte_vectors():
+    # an input 8 bytes off 16-byte alignment gives 8-byte vectors: no ticket kernel
+    got, msg = status_of(ag.plan_all_gather_ex, geom(), 8, 0, 1, INPUT + 8, 0, 1024, 4096, "f16", 0, 0, 0,
+                         tile_order="tickets")
+    assert got == ag.AG_ERR_UNSUPPORTED and "ticket" in msg
+    p = ag.plan_all_gather(_big_geom(), 8, 0, 1, INPUT + 8, 0, 16384, 8192, "f16", 0, 0, 256)
+    assert p.vec_bytes == 8 and p.tile_order == ag.AG_ORDER_STRIDE
+
+
+def test_plan_all_to_all_takes_no_tile_order():
+    got, _ = status_of(ag.plan_all_to_all_ex, geom(), 8, 0, 1, INPUT, 0, 128, 4096, "f16", 0, 0, 0,
+                       tile_order="tickets")
+    assert got == ag.AG_ERR_INVALID_ARG
+    p = ag.plan_all_to_all(geom(), 8, 0, 1, INPUT, 0, 1024, 4096, "f16", 0, 0, 256)
+    assert p.tile_order == ag.AG_ORDER_STRIDE and p.tiles_per_ticket == 0

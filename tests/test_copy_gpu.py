@@ -339,7 +339,8 @@ def test_launching_entry_point_rejects_invalid_arguments():
 # full-size workloads: W=8, 16384 x 8192 per rank
 # ---------------------------------------------------------------------------
 
-def _full_size(dtype, W, start, stride, M, N, programs_list, seed):
+def _full_size(dtype, W, start, stride, M, N, programs_list, seed, orders=("auto", "stride")):
+    """Each program count in the library's tile order (tickets at this size) and in the grid stride."""
     require_gpu()
     e = E[dtype]
     blk = M * N * e
@@ -353,10 +354,18 @@ def _full_size(dtype, W, start, stride, M, N, programs_list, seed):
     expect = to_device(all_gather_expected_block(ins))       # oracle's gathered block, uploaded for comparison
     th = TorchHeap(R, S)
     try:
-        for programs in programs_list:
+        for programs, order in itertools.product(programs_list, orders):
             th.fill(gen.SENTINEL16)
-            log(f"  n_programs={programs}")
-            run_all_gather(th, dev, W, start, stride, guard, M, N, dtype, 8, 256, programs)
+            p = ag.plan_all_gather_ex(th.view(start).geometry(), W, start, stride, dev[0], guard, M, N, dtype, 8, 256,
+                                      programs, tile_order=order)
+            log(f"  n_programs={programs} order={order} -> tile_order {p.tile_order}, {p.tiles_per_ticket} per ticket")
+            if order == "auto":
+                assert p.tile_order == ag.AG_ORDER_TICKETS
+                run_all_gather(th, dev, W, start, stride, guard, M, N, dtype, 8, 256, programs)
+            else:
+                for j in range(W):
+                    ag.all_gather_ex(th.view(start + j * stride), W, start, stride, dev[j], guard, M, N, dtype, 8, 256,
+                                     programs, tile_order=order)
             torch.cuda.synchronize()
             sentinel = torch.tensor([np.int16(np.uint16(gen.SENTINEL16).view(np.int16))], device="cuda")
             for r in range(R):

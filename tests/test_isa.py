@@ -181,6 +181,35 @@ def test_all_to_all_kernel_hoists_bases_and_pipelines_tiles(asm, vec, w, vpt):
     assert _meta(asm["ag_copy.hip"], sym)["scratch"] == 0
 
 
+@pytest.mark.parametrize("w,vpt,g,wide", [("8", "1", "4", "1"), ("8", "1", "8", "1"), ("8", "1", "16", "0"),
+                                          ("8", "2", "8", "0"), ("4", "1", "4", "1"), ("1", "2", "4", "1")])
+def test_ticket_kernel_hoists_bases_and_never_drains_before_a_store(asm, w, vpt, g, wide):
+    """Ticket order: the table is read once before the tile loop; the counter is an atomic increment
+    (not an add, which the compiler would wait for at once); no store is preceded by a full drain."""
+    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_copy_ticket_kernelILi16ELi{w}ELi{vpt}ELi{g}ELb{wide}E")
+    W, VPT, G = int(w), int(vpt), int(g)
+    h, b = _outermost(_loops(lines))
+    body, prologue = lines[h:b + 1], lines[:h]
+    assert sum(ln.startswith("global_load_dwordx2") for ln in prologue) == 1      # the table, once
+    assert not any(ln.startswith("global_load") for ln in body)
+    # the only scalar loads the loop may hold re-read kernel arguments (the counter's address, at
+    # offset 0x60 of the argument block) where the compiler rematerialises instead of keeping a register
+    assert all(re.match(r"s_load_dwordx2 s\[\d+:\d+\], s\[\d+:\d+\], 0x60$", ln)
+               for ln in body if ln.startswith("s_load")), [ln for ln in body if ln.startswith("s_load")]
+    assert sum(ln.startswith("v_readlane_b32") for ln in prologue) >= 2 * W
+    incs = [ln for ln in lines if ln.startswith("global_atomic_inc")]
+    assert len(incs) >= 3 and not any(ln.startswith("global_atomic_add ") and "offset:4" not in ln for ln in lines)
+    loads = [ln for ln in body if re.match(r"buffer_load", ln)]
+    stores = [i for i, ln in enumerate(body) if ln.startswith("buffer_store")]
+    assert len(loads) == 2 * G * VPT and len(stores) == 2 * G * W * VPT    # two batches per unrolled trip
+    prev = 0
+    for i in stores:
+        assert not [ln for ln in body[prev:i] if ln.startswith("s_waitcnt") and "vmcnt(0)" in ln], body[prev:i]
+        prev = i
+    assert not _sign_extended_lane_reads(lines)
+    assert _meta(asm["ag_copy.hip"], sym)["scratch"] == 0
+
+
 _SIGN_OPS = ("s_ashr_i32", "s_ashr_i64", "s_bfe_i32", "s_bfe_i64", "s_sext_i32_i8", "s_sext_i32_i16",
              "v_ashrrev_i32", "v_ashrrev_i64", "v_bfe_i32")
 

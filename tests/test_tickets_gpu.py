@@ -1,0 +1,155 @@
+"""Parity of the all-gather in ticket order (AG_ORDER_TICKETS) with the CPU oracle.
+
+The tile order changes which program copies which tile and when, never the
+result: every case compares the whole heap with the oracle byte for byte
+(outputs, guards, regions outside the group).  The per-rank tile counters must
+be back at zero after every call (the last program to finish resets them).
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from gemm_all_gather_amd import binding as ag
+from gemm_all_gather_amd import inputs as gen
+from oracle import all_gather_oracle
+from tests.gpu_util import TorchHeap, log, require_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+E = {"f16": 2, "bf16": 2, "f32": 4}
+
+
+def _counters(th: TorchHeap) -> np.ndarray:
+    """The heap's per-rank tile counters (two words in a 64-byte block per rank, after the base table)."""
+    info = th.heap.info()
+    n = info["n_ranks"]
+    start = info["base_table"] + -(-8 * n // 256) * 256
+
+    class _C:
+        __cuda_array_interface__ = {"shape": (n * 16,), "typestr": "<u4", "data": (start, False), "version": 3,
+                                    "strides": None}
+
+    torch.cuda.synchronize()
+    return torch.as_tensor(_C(), device="cuda").cpu().numpy().reshape(n, 16)[:, :2]
+
+
+def _run(th, dev, W, start, stride, off, M, N, dtype, tile, programs, order="tickets", stream=None):
+    for j in range(W):
+        ag.all_gather_ex(th.view(start + j * stride), W, start, stride, dev[j], off, M, N, dtype, tile[0], tile[1],
+                         programs, tile_order=order, stream=stream)
+
+
+def _check(th, before, ins, S, start, stride, off):
+    got = th.host()
+    want = all_gather_oracle(before, S, ins, start, stride, off)
+    if not np.array_equal(got, want):
+        bad = np.flatnonzero(got != want)
+        raise AssertionError(f"{bad.size} bytes differ; first at region {bad[0] // S} offset {bad[0] % S}")
+    assert not _counters(th).any(), "a tile counter was left non-zero"
+    return got
+
+
+_CASES = []
+_rng = np.random.default_rng(31)
+for W, (start, stride), M, N in itertools.product([1, 2, 3, 5, 8], [(0, 1), (1, 2), (3, 1)], [1, 7, 64, 300, 1000],
+                                                  [256, 264, 520, 4104]):
+    if start + (W - 1) * stride >= 8:
+        continue
+    _CASES.append((W, start, stride, M, N))
+_CASES = [c for c in _CASES if _rng.random() < 0.4]
+
+
+@pytest.mark.parametrize("W,start,stride,M,N", _CASES)
+def test_ticket_order_sweep(W, start, stride, M, N):
+    require_gpu()
+    rng = np.random.default_rng([W, start, stride, M, N, 5])
+    dtype = ["f16", "bf16", "f32"][int(rng.integers(0, 3))]
+    e = E[dtype]
+    # one or two 16-byte vectors per thread and tile
+    tiles = [(8, 256), (4, 512), (16, 128), (1, 2048), (8, 512), (16, 256)] if e == 2 else \
+        [(8, 256), (4, 256), (2, 512), (1, 1024)]
+    tile = tiles[int(rng.integers(0, len(tiles)))]
+    programs = [1, 3, 7, 64, 256, 10_000][int(rng.integers(0, 6))]
+    off = 16 * int(rng.integers(0, 8))
+    S = ((off + W * M * N * e + 300) // 256 + 1) * 256
+    log(f"tickets W={W} group=({start},{stride}) M={M} N={N} {dtype} tile={tile} programs={programs} off={off}")
+    th = TorchHeap(8, S)
+    try:
+        ins = [gen.uniform_pm1((M, N), dtype, W * 100 + M, j) for j in range(W)]
+        dev = [to_device(x) for x in ins]
+        p = ag.plan_all_gather_ex(th.view(start).geometry(), W, start, stride, dev[0], off, M, N, dtype, *tile,
+                                  programs, tile_order="tickets")
+        assert p.tile_order == ag.AG_ORDER_TICKETS and p.tiles_per_ticket in (4, 8, 16)
+        before = th.host()
+        _run(th, dev, W, start, stride, off, M, N, dtype, tile, programs)
+        _check(th, before, ins, S, start, stride, off)
+    finally:
+        th.close()
+
+
+def test_ticket_order_repeated_calls_and_counter_reset():
+    """The same call again and again, then other ranks and shapes: the counters are zero between calls."""
+    require_gpu()
+    W, M, N, dtype = 8, 777, 1024, "bf16"
+    S = ((W * M * N * 2 + 4096) // 256 + 1) * 256
+    th = TorchHeap(8, S)
+    try:
+        ins = [gen.uniform_pm1((M, N), dtype, 61, j) for j in range(W)]
+        dev = [to_device(x) for x in ins]
+        before = th.host()
+        for programs in (5, 5, 5, 256, 64, 1, 300):
+            log(f"tickets repeated: programs={programs}")
+            for j in (3, 3, 0, 7, 1, 2, 4, 5, 6):
+                ag.all_gather_ex(th.view(j), W, 0, 1, dev[j], 0, M, N, dtype, 8, 256, programs, tile_order="tickets")
+            assert not _counters(th).any()
+        _check(th, before, ins, S, 0, 1, 0)
+    finally:
+        th.close()
+
+
+def test_ticket_order_concurrent_ranks_on_streams():
+    """Different ranks' calls on four streams at once (each rank has its own counter)."""
+    require_gpu()
+    W, M, N, dtype = 8, 2048, 2048, "f16"
+    S = ((W * M * N * 2 + 4096) // 256 + 1) * 256
+    th = TorchHeap(8, S)
+    try:
+        ins = [gen.uniform_pm1((M, N), dtype, 62, j) for j in range(W)]
+        dev = [to_device(x) for x in ins]
+        before = th.host()
+        streams = [torch.cuda.Stream() for _ in range(4)]
+        torch.cuda.synchronize()
+        log("tickets on four streams")
+        for j in range(W):
+            ag.all_gather_ex(th.view(j), W, 0, 1, dev[j], 0, M, N, dtype, 8, 256, 64, tile_order="tickets",
+                             stream=streams[j % 4])
+        torch.cuda.synchronize()
+        _check(th, before, ins, S, 0, 1, 0)
+    finally:
+        th.close()
+
+
+def test_ticket_order_in_place_and_random_bit_patterns():
+    require_gpu()
+    W, M, N = 4, 300, 776
+    S = ((W * M * N * 4 + 1024) // 256 + 1) * 256
+    th = TorchHeap(4, S)
+    try:
+        before = th.fill_random(63)
+        ins = [gen.random_bit_patterns((M, N), 4, 64, j) for j in range(W)]
+        blk = M * N * 4
+        # rank j's input already sits in its own slot of its own region (in place)
+        for j in range(W):
+            th.region(j)[j * blk:(j + 1) * blk].copy_(torch.from_numpy(ins[j].view(np.uint8).reshape(-1)))
+        torch.cuda.synchronize()
+        before = th.host()
+        log("tickets in place, fp32 bit patterns")
+        for j in range(W):
+            ag.all_gather_ex(th.view(j), W, 0, 1, th.heap.rank_ptr(j, j * blk), 0, M, N, "f32", 8, 256, 16,
+                             tile_order="tickets")
+        _check(th, before, ins, S, 0, 1, 0)
+    finally:
+        th.close()
