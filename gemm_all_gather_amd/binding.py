@@ -24,6 +24,7 @@ AG_F16, AG_BF16, AG_F32 = 0, 1, 2
 DTYPE_CODES = {"f16": AG_F16, "bf16": AG_BF16, "f32": AG_F32}
 ELEM_BYTES = {"f16": 2, "bf16": 2, "f32": 4}
 AG_MAX_WORLD = 8
+AG_NOALLOC_MAX_RANKS = 64
 AG_REGION_ALIGN = 2 << 20
 
 
@@ -105,6 +106,8 @@ _SIGNATURES = {
                          _c_int, ctypes.POINTER(CopyOptions), _vp],
     "ag_plan_all_gather_ex": [ctypes.POINTER(Geometry), _c_int, _c_int, _c_int, _c_u64, _c_size, _c_i64, _c_i64,
                               _c_int, _c_int, _c_int, _c_int, ctypes.POINTER(CopyOptions), ctypes.POINTER(Plan)],
+    "ag_all_gather_noalloc": [_vp, _c_int, _c_int, _c_int, _vp, _c_size, _c_i64, _c_i64, _c_int, _c_int, _c_int,
+                              _c_int, ctypes.POINTER(CopyOptions), _vp],
     "ag_all_to_all": [_vp, _c_int, _c_int, _c_int, _vp, _c_size, _c_i64, _c_i64, _c_int, _c_int, _c_int,
                       _c_int, _vp],
     "ag_plan_all_to_all": [ctypes.POINTER(Geometry), _c_int, _c_int, _c_int, _c_u64, _c_size, _c_i64, _c_i64,
@@ -289,6 +292,16 @@ def all_gather_ex(heap: Heap, W, rank_start, rank_stride, input, out_offset, M_l
     _check(lib().ag_all_gather_ex(heap.handle, W, rank_start, rank_stride, _ptr(input), out_offset, M_local, N,
                                   _dtype(dtype), tile_m, tile_n, n_programs, ctypes.byref(o), _stream(stream)),
            "ag_all_gather_ex")
+
+
+def all_gather_noalloc(heap: Heap, W, rank_start, rank_stride, input, out_offset, M_local, N, dtype,
+                       tile_m=0, tile_n=0, n_programs=0, dest_group=0, schedule=0, stream=None,
+                       tile_order=0) -> None:
+    """ag_all_gather_noalloc: ag_all_gather_ex whose tile counter is the library's fixed device array."""
+    o = _options(dest_group, schedule, tile_order)
+    _check(lib().ag_all_gather_noalloc(heap.handle, W, rank_start, rank_stride, _ptr(input), out_offset, M_local, N,
+                                       _dtype(dtype), tile_m, tile_n, n_programs, ctypes.byref(o), _stream(stream)),
+           "ag_all_gather_noalloc")
 
 
 def plan_all_to_all(geom: Geometry, W, rank_start, rank_stride, input_addr, out_offset, M_chunk, N, dtype,

@@ -45,6 +45,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "ag_internal.h"
 
 namespace ag {
@@ -738,6 +740,52 @@ bool copy_supported(int kind, int vec_bytes, int dests, int group, int vpt, bool
 bool copy_ticket_supported(int vec_bytes, int dests, int vpt, int ticket)
 {
     return pick_ticket(vec_bytes, dests, vpt, ticket, false) != nullptr;
+}
+
+// ---- tile counters of the allocation-free entry point: a fixed device array, one 64-byte block
+// (16 words, two used) per rank index, zero-initialised when the code object is loaded.  Host code
+// reaches it only through the address hipGetSymbolAddress reports for the current device (the
+// array's name is a host-side stand-in, not a device address).
+static __device__ __align__(256) uint32_t scratch[kNoAllocMaxRanks * 16];
+
+namespace {
+constexpr int kNoAllocMaxDevices = 64;
+
+// Zeroes one rank's counter pair at the start of a call (a kernel, not a memset: the call may be
+// captured into a graph, and replays must clear it too).
+__global__ __launch_bounds__(64) void clear_tickets_kernel(uint32_t* counter)
+{
+    if (threadIdx.x < 2) counter[threadIdx.x] = 0u;
+}
+}  // namespace
+
+hipError_t noalloc_tickets(int rank, hipStream_t stream, uint32_t** out)
+{
+    if (rank < 0 || rank >= kNoAllocMaxRanks) return hipErrorInvalidValue;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kNoAllocMaxDevices) return hipErrorInvalidDevice;
+    static std::mutex mu;
+    static uint32_t* base[kNoAllocMaxDevices] = {};
+    uint32_t* b = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (base[dev] == nullptr) {   // once per device, with that device current
+            void* p = nullptr;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (p == nullptr) return hipErrorInvalidSymbol;
+            base[dev] = static_cast<uint32_t*>(p);
+        }
+        b = base[dev];
+    }
+    uint32_t* counter = b + 16 * static_cast<size_t>(rank);
+    hipLaunchKernelGGL(clear_tickets_kernel, dim3(1), dim3(64), 0, stream, counter);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    *out = counter;
+    return hipSuccess;
 }
 
 hipError_t launch_copy(const CopyLaunch& l, hipStream_t stream)

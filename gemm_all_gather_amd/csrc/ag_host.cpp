@@ -21,6 +21,8 @@
 #include "ag.h"
 #include "ag_internal.h"
 
+static_assert(AG_NOALLOC_MAX_RANKS == ag::kNoAllocMaxRanks, "one limit for the allocation-free entry point");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -591,11 +593,16 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     return ok();
 }
 
+// noalloc: the ticket order's counter comes from the library's fixed device array (ag_all_gather_noalloc)
 ag_status_t launch_copy_call(const ag_heap_t* heap, int kind, int W, int rank_start, int rank_stride,
                              const void* input, size_t out_offset, int64_t M, int64_t N, ag_dtype_t dtype,
-                             int tile_m, int tile_n, int n_programs, const ag_copy_options_t* options, void* stream)
+                             int tile_m, int tile_n, int n_programs, const ag_copy_options_t* options, void* stream,
+                             bool noalloc = false)
 {
     if (!heap) return fail(AG_ERR_INVALID_ARG, "heap is NULL");
+    if (noalloc && heap->core->n_ranks > AG_NOALLOC_MAX_RANKS)
+        return fail(AG_ERR_UNSUPPORTED, "ag_all_gather_noalloc keeps tile counters for heaps of at most %d ranks "
+                    "(this heap has %d)", AG_NOALLOC_MAX_RANKS, heap->core->n_ranks);
     ag_heap_geometry_t geom;
     ag_heap_geometry(heap, &geom);
     ag_plan_t p;
@@ -645,6 +652,10 @@ ag_status_t launch_copy_call(const ag_heap_t* heap, int kind, int W, int rank_st
     l.args.tickets = p.tiles_per_ticket
                          ? heap->core->tickets + (kTicketBytes / sizeof(uint32_t)) * static_cast<uint64_t>(geom.rank)
                          : nullptr;
+    if (noalloc && p.tiles_per_ticket) {
+        const hipError_t e1 = ag::noalloc_tickets(geom.rank, static_cast<hipStream_t>(stream), &l.args.tickets);
+        if (e1 != hipSuccess) return fail_hip(e1, "tile counter of the allocation-free entry point");
+    }
     const hipError_t e2 = ag::launch_copy(l, static_cast<hipStream_t>(stream));
     if (e2 != hipSuccess) return fail_hip(e2, kind == ag::kCopyAllToAll ? "all-to-all kernel launch" : "all-gather kernel launch");
     return ok();
@@ -703,6 +714,15 @@ ag_status_t ag_all_gather_ex(const ag_heap_t* heap, int W, int rank_start, int r
 {
     return launch_copy_call(heap, ag::kCopyAllGather, W, rank_start, rank_stride, input, out_offset, M_local, N,
                             dtype, tile_m, tile_n, n_programs, options, stream);
+}
+
+ag_status_t ag_all_gather_noalloc(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                                  const void* input, size_t out_offset, int64_t M_local, int64_t N,
+                                  ag_dtype_t dtype, int tile_m, int tile_n, int n_programs,
+                                  const ag_copy_options_t* options, void* stream)
+{
+    return launch_copy_call(heap, ag::kCopyAllGather, W, rank_start, rank_stride, input, out_offset, M_local, N,
+                            dtype, tile_m, tile_n, n_programs, options, stream, true);
 }
 
 ag_status_t ag_all_to_all(const ag_heap_t* heap, int W, int rank_start, int rank_stride,

@@ -52,6 +52,12 @@ bool copy_supported(int kind, int vec_bytes, int dests, int group, int vpt, bool
 bool copy_ticket_supported(int vec_bytes, int dests, int vpt, int ticket);
 hipError_t launch_copy(const CopyLaunch& l, hipStream_t stream);
 
+// Tile counters of ag_all_gather_noalloc: rank indices below kNoAllocMaxRanks have a counter pair in a
+// fixed device array of the library (no allocation).  noalloc_tickets returns the current device's
+// counter of a rank, after enqueueing on stream a small kernel that zeroes it.
+constexpr int kNoAllocMaxRanks = 64;
+hipError_t noalloc_tickets(int rank, hipStream_t stream, uint32_t** out);
+
 // Arguments of the fused GEMM + multi-destination store kernel.
 struct GemmKernelArgs {
     const uint64_t* heap_bases;

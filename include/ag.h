@@ -286,6 +286,26 @@ ag_status_t ag_plan_all_gather_ex(const ag_heap_geometry_t* geom, int W, int ran
                                   const ag_copy_options_t* options, ag_plan_t* plan);
 
 /* ------------------------------------------------------------------------
+ * ag_all_gather_ex for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, result, errors and kernels as
+ * ag_all_gather_ex; it calls no allocating routine.  The only device memory
+ * it uses beyond the input and the heap is the ticket order's tile counter,
+ * which here lives in a fixed device array of the library (one counter per
+ * rank index, AG_NOALLOC_MAX_RANKS of them, 4 KiB per GPU, held until the
+ * process ends) instead of in the heap; each call first zeroes the calling
+ * rank's counter with a small kernel on stream.  Heaps of more than
+ * AG_NOALLOC_MAX_RANKS ranks give AG_ERR_UNSUPPORTED.  Every call on a GPU
+ * shares that GPU's array: calls that overlap in time and use the same
+ * rank index race, whichever heaps they use.
+ * ------------------------------------------------------------------------ */
+#define AG_NOALLOC_MAX_RANKS 64
+ag_status_t ag_all_gather_noalloc(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
+                                  const void* input, size_t out_offset, int64_t M_local, int64_t N,
+                                  ag_dtype_t dtype, int tile_m, int tile_n, int n_programs,
+                                  const ag_copy_options_t* options, void* stream);
+
+/* ------------------------------------------------------------------------
  * All-to-all on the same heap and destination machinery (ROCm/iris #594,
  * "Compiler inspection and grouping", and ROCm/iris #591, "Hoist the peer
  * heap bases": the all_to_all collective has the same per-destination
