@@ -50,7 +50,8 @@ class Plan(ctypes.Structure):
                 ("rank_block_offset", ctypes.c_uint64), ("bytes_read", ctypes.c_uint64),
                 ("bytes_written", ctypes.c_uint64), ("flops", ctypes.c_double),
                 ("dest_group", ctypes.c_int32), ("schedule", ctypes.c_int32),
-                ("tile_order", ctypes.c_int32), ("tiles_per_ticket", ctypes.c_int32)]
+                ("tile_order", ctypes.c_int32), ("tiles_per_ticket", ctypes.c_int32),
+                ("ticket_wait", ctypes.c_int32), ("reserved_plan", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

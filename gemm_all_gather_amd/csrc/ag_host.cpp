@@ -195,6 +195,20 @@ ag_status_t check_group(const ag_heap_geometry_t* geom, int W, int rank_start, i
 #ifndef AG_COPY_NARROW_SLICES
 #define AG_COPY_NARROW_SLICES 4
 #endif
+// Ticket order (tile_order AG_ORDER_AUTO): tiles per ticket at >= 256, >= 128 and fewer programs, and
+// the tiles per program from which the library chooses tickets over the grid stride.
+#ifndef AG_TICKETS_G_WIDE
+#define AG_TICKETS_G_WIDE 4
+#endif
+#ifndef AG_TICKETS_G_MID
+#define AG_TICKETS_G_MID 8
+#endif
+#ifndef AG_TICKETS_G_NARROW
+#define AG_TICKETS_G_NARROW 16
+#endif
+#ifndef AG_TICKETS_MIN_TILES_PER_PROGRAM
+#define AG_TICKETS_MIN_TILES_PER_PROGRAM 64
+#endif
 constexpr int kCopyMaxVpt = 8;
 constexpr int kCopyMaxSlices = AG_COPY_MAX_SLICES;
 constexpr uint64_t kCopyNarrowSlices = AG_COPY_NARROW_SLICES;   // launches on fewer than half the CUs
@@ -547,7 +561,7 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     int ticket = 0;
     {
         const int tvpt = static_cast<int>(tile_vecs / 256);
-        int g = programs >= 256 ? 4 : programs >= 128 ? 8 : 16;
+        int g = programs >= 256 ? AG_TICKETS_G_WIDE : programs >= 128 ? AG_TICKETS_G_MID : AG_TICKETS_G_NARROW;
         if (tvpt == 2 && g > 8) g = 8;
         const bool fits = !part && !a2a && p.dest_group == 0 && ag::copy_ticket_supported(vec, W, tvpt, g);
         if (opt.tile_order == AG_ORDER_TICKETS) {
@@ -555,7 +569,7 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
                 return fail(AG_ERR_UNSUPPORTED, "no ticket-order kernel for this call (%d-byte vectors, %d per thread, "
                             "destination group %d)", vec, tvpt, p.dest_group);
             ticket = g;
-        } else if (opt.tile_order == AG_ORDER_AUTO && fits && total >= 64 * programs) {
+        } else if (opt.tile_order == AG_ORDER_AUTO && fits && total >= AG_TICKETS_MIN_TILES_PER_PROGRAM * programs) {
             ticket = g;
         }
     }
@@ -589,6 +603,8 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     p.variant = kind;
     p.tile_order = ticket ? AG_ORDER_TICKETS : AG_ORDER_STRIDE;
     p.tiles_per_ticket = ticket;
+    // with at least one program per CU, each program waits for a ticket's stores before the next one's
+    p.ticket_wait = (ticket && grid >= static_cast<uint64_t>(geom->num_cus)) ? 1 : 0;
     *plan = p;
     return ok();
 }
@@ -649,6 +665,7 @@ ag_status_t launch_copy_call(const ag_heap_t* heap, int kind, int W, int rank_st
     l.wide = (p.dest_group == 0 && 2 * static_cast<int64_t>(p.n_programs) >= geom.num_cus) ? 1 : 0;
     // ticket order: the calling rank's counter (zero between calls; calls of one rank never overlap)
     l.ticket = p.tiles_per_ticket;
+    l.drain = p.ticket_wait;
     l.args.tickets = p.tiles_per_ticket
                          ? heap->core->tickets + (kTicketBytes / sizeof(uint32_t)) * static_cast<uint64_t>(geom.rank)
                          : nullptr;

@@ -465,12 +465,13 @@ def _big_geom(e=2, **kw):
     return geom(bytes_per_rank=8 * 16384 * 8192 * e + MiB, **kw)
 
 
-@pytest.mark.parametrize("progs,ticket", [(256, 4), (0, 4), (128, 8), (64, 16)])
-def test_plan_tickets_for_long_calls(progs, ticket):
+@pytest.mark.parametrize("progs,ticket,wait", [(256, 4, 1), (0, 4, 1), (512, 4, 1), (128, 8, 0), (64, 16, 0)])
+def test_plan_tickets_for_long_calls(progs, ticket, wait):
     p = plan(g=_big_geom(), progs=progs, **BIG)
     assert p.tile_order == ag.AG_ORDER_TICKETS and p.tiles_per_ticket == ticket
     assert p.threads == 256 and p.n_programs == (progs or 256)
     assert p.total_tiles == 2048 * 32 and p.vectors_per_thread == 1
+    assert p.ticket_wait == wait               # one program per CU or more: a wait after every ticket
 
 
 def test_plan_tickets_two_vectors_per_thread_at_most_eight():

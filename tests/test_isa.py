@@ -181,12 +181,16 @@ def test_all_to_all_kernel_hoists_bases_and_pipelines_tiles(asm, vec, w, vpt):
     assert _meta(asm["ag_copy.hip"], sym)["scratch"] == 0
 
 
-@pytest.mark.parametrize("w,vpt,g,wide", [("8", "1", "4", "1"), ("8", "1", "8", "1"), ("8", "1", "16", "0"),
-                                          ("8", "2", "8", "0"), ("4", "1", "4", "1"), ("1", "2", "4", "1")])
-def test_ticket_kernel_hoists_bases_and_never_drains_before_a_store(asm, w, vpt, g, wide):
+@pytest.mark.parametrize("w,vpt,g,wide,drain", [("8", "1", "4", "1", "1"), ("8", "1", "4", "1", "0"),
+                                                ("8", "1", "8", "1", "0"), ("8", "1", "16", "0", "0"),
+                                                ("8", "2", "8", "0", "0"), ("4", "1", "4", "1", "1"),
+                                                ("1", "2", "4", "1", "0")])
+def test_ticket_kernel_hoists_bases_and_never_drains_before_a_store(asm, w, vpt, g, wide, drain):
     """Ticket order: the table is read once before the tile loop; the counter is an atomic increment
-    (not an add, which the compiler would wait for at once); no store is preceded by a full drain."""
-    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_copy_ticket_kernelILi16ELi{w}ELi{vpt}ELi{g}ELb{wide}E")
+    (not an add, which the compiler would wait for at once); no store within a ticket's G*W stores is
+    preceded by a full drain, and between tickets there is one only where the launch asks for it."""
+    sym, lines = _kernel_body(asm["ag_copy.hip"],
+                              f"ag_copy_ticket_kernelILi16ELi{w}ELi{vpt}ELi{g}ELb{wide}ELb{drain}E")
     W, VPT, G = int(w), int(vpt), int(g)
     h, b = _outermost(_loops(lines))
     body, prologue = lines[h:b + 1], lines[:h]
@@ -202,10 +206,16 @@ def test_ticket_kernel_hoists_bases_and_never_drains_before_a_store(asm, w, vpt,
     loads = [ln for ln in body if re.match(r"buffer_load", ln)]
     stores = [i for i, ln in enumerate(body) if ln.startswith("buffer_store")]
     assert len(loads) == 2 * G * VPT and len(stores) == 2 * G * W * VPT    # two batches per unrolled trip
-    prev = 0
-    for i in stores:
-        assert not [ln for ln in body[prev:i] if ln.startswith("s_waitcnt") and "vmcnt(0)" in ln], body[prev:i]
-        prev = i
+    per_batch = G * W * VPT
+    for k, i in enumerate(stores):
+        prev = stores[k - 1] if k else 0
+        drains = [ln for ln in body[prev:i] if ln.startswith("s_waitcnt") and "vmcnt(0)" in ln]
+        if k % per_batch:                      # inside one ticket's run of stores: never
+            assert not drains, body[prev:i]
+        elif k and drain == "0":               # between tickets: only the draining variant waits
+            assert not drains, body[prev:i]
+        elif k and drain == "1":
+            assert len(drains) == 1, body[prev:i]
     assert not _sign_extended_lane_reads(lines)
     assert _meta(asm["ag_copy.hip"], sym)["scratch"] == 0
 
