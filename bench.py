@@ -284,6 +284,25 @@ def _context(args, stream, timed, head):
     ctx["all_gather_1024x4096_f16_cache_assisted_GBs_by_programs"] = sm
     small.close()
 
+    ctx["all_to_all"] = _all_to_all(sub, stream, timed)
+
+    # the edge shapes: rows of 4100 elements (partial last column tile); the strided group of ranks
+    # 1, 3, 5, 7 (W=4) at both sizes
+    edges = {}
+    for name, M, N, W, start, stride, seed in (("1000x4100_f16_W8", 1000, 4100, AG_W, 0, 1, 7),
+                                               ("1000x4100_f16_W4_group_1_2", 1000, 4100, 4, 1, 2, 8),
+                                               ("16384x8192_f16_W4_group_1_2", 16384, 8192, 4, 1, 2, 9)):
+        wl = _Workload(M, N, "f16", W=W, start=start, stride=stride, seed=seed)
+        edges[name] = rate(wl, programs=256)[0]
+        wl.close()
+    ctx["all_gather_edges_GBs"] = edges
+    return ctx
+
+
+def _all_to_all(sub, stream, timed):
+    """The all-to-all on its own heap: W=8, 8 chunks of 1024x4096 fp16 per rank, tile and partitioned schedules."""
+    from gemm_all_gather_amd import binding as ag
+
     # all-to-all: each rank sends 8 chunks of 1024x4096 fp16 (64 MiB per rank); 8x512 tiles, two 16-byte
     # vectors per thread (measured 5.3 TB/s against 5.0 for 8x256 at 256 programs)
     A2A_TILE = (8, 512)
@@ -297,7 +316,7 @@ def _context(args, stream, timed, head):
                            for j in range(AG_W)], sub)
     a2a_bytes = a2a_plan.bytes_read + a2a_plan.bytes_written
     launch_s = ms / 1e3 / AG_W
-    ctx["all_to_all"] = {
+    res = {
         "workload": f"all-to-all W={AG_W}, {AG_W} chunks of {mc}x{n} fp16 per rank, tile {A2A_TILE[0]}x{A2A_TILE[1]}, "
                     f"{a2a_plan.n_programs} programs (8 calls per job)",
         "value": round(AG_W * a2a_bytes / (ms / 1e3) / 1e9, 1), "unit": "GB/s",
@@ -309,20 +328,9 @@ def _context(args, stream, timed, head):
     # the partitioned schedule of the same exchange (program p copies one chunk to destination p mod W)
     ms, _ = timed(lambda: [ag.all_to_all_ex(views[j], AG_W, 0, 1, a2a_in[j], 0, mc, n, "f16", 16, 512, 256,
                                             schedule="partitioned", stream=stream) for j in range(AG_W)], sub)
-    ctx["all_to_all"]["partitioned_16x512_256_programs_GBs"] = round(AG_W * a2a_bytes / (ms / 1e3) / 1e9, 1)
+    res["partitioned_16x512_256_programs_GBs"] = round(AG_W * a2a_bytes / (ms / 1e3) / 1e9, 1)
     a2a.close()
-
-    # the edge shapes: rows of 4100 elements (partial last column tile); the strided group of ranks
-    # 1, 3, 5, 7 (W=4) at both sizes
-    edges = {}
-    for name, M, N, W, start, stride, seed in (("1000x4100_f16_W8", 1000, 4100, AG_W, 0, 1, 7),
-                                               ("1000x4100_f16_W4_group_1_2", 1000, 4100, 4, 1, 2, 8),
-                                               ("16384x8192_f16_W4_group_1_2", 16384, 8192, 4, 1, 2, 9)):
-        wl = _Workload(M, N, "f16", W=W, start=start, stride=stride, seed=seed)
-        edges[name] = rate(wl, programs=256)[0]
-        wl.close()
-    ctx["all_gather_edges_GBs"] = edges
-    return ctx
+    return res
 
 
 def _context_fused(args, stream, timed, views, fu_off):
@@ -413,8 +421,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-m", type=int, default=FU_M, help="M_local of the fused workload (16384 or 1024)")
-    ap.add_argument("--only", choices=["all", "copy", "fused"], default="all",
-                    help="restrict the timed step to one kernel (profiling runs)")
+    ap.add_argument("--only", choices=["all", "copy", "fused", "a2a"], default="all",
+                    help="restrict the timed step to one kernel (profiling runs); a2a times the all-to-all "
+                         "context workload alone")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context measurements (program counts and element types, variants, the "
                          "1024x4096 all-gather, all-to-all, edge shapes, the other fused workloads, plain "
@@ -436,6 +445,27 @@ def main() -> int:
     ag.lib()
     dev_props = torch.cuda.get_device_properties(0)
     stream = torch.cuda.current_stream()
+
+    if args.only == "a2a":   # profiling run of the all-to-all workload alone
+        def timed_a2a(job, a):
+            for _ in range(a.warmup):
+                job()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(a.steps):
+                job()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / a.steps, 0.0
+        res = _all_to_all(args, stream, timed_a2a)
+        if args.calib_copy_mib > 0:
+            src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+            torch.empty_like(src).copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps({"metric": "all-to-all HBM GB/s", "value": res["value"], "unit": "GB/s", "n_gpus": 1,
+                          "steps": args.steps, "warmup": args.warmup, "all_to_all": res}), flush=True)
+        return 0
 
     # ---------------- all-gather setup: 16384 x 8192 fp16 per rank, 8 regions of 2 GiB
     head = _Workload(AG_M, AG_N, AG_DTYPE, seed=1) if args.only != "fused" else None
@@ -547,7 +577,8 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(per_call_bytes / copy_launch_s / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": _traffic(f"ag_copy_kernel_w8_{AG_M}x{AG_N}_f16_pmc.md", "ag_copy.hip", per_call_bytes),
+            "traffic": _traffic(f"{'ag_copy_ticket_kernel' if ag_plan.tile_order == ag.AG_ORDER_TICKETS else 'ag_copy_kernel'}"
+                                f"_w8_{AG_M}x{AG_N}_f16_pmc.md", "ag_copy.hip", per_call_bytes),
             "kernel": (f"ag_copy_ticket_kernel<VEC={ag_plan.vec_bytes},W={AG_W},VPT={ag_plan.vectors_per_thread},"
                        f"G={ag_plan.tiles_per_ticket}>" if ag_plan.tile_order == ag.AG_ORDER_TICKETS else
                        f"ag_copy_kernel<VEC={ag_plan.vec_bytes},W={AG_W},VPT={ag_plan.vectors_per_thread}>"),
