@@ -559,15 +559,19 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     // round trip per ticket, which long calls hide and short ones do not (at 1024x4096 fp16, W=8,
     // 16 tiles per program: 15.9 against 11.8 us per call).
     int ticket = 0;
+    const int tvpt = static_cast<int>(tile_vecs / 256);   // 16-byte vectors per thread and tile (tickets)
     {
-        const int tvpt = static_cast<int>(tile_vecs / 256);
         int g = programs >= 256 ? AG_TICKETS_G_WIDE : programs >= 128 ? AG_TICKETS_G_MID : AG_TICKETS_G_NARROW;
         if (tvpt == 2 && g > 8) g = 8;
-        const bool fits = !part && !a2a && p.dest_group == 0 && ag::copy_ticket_supported(vec, W, tvpt, g);
+        // the ticket kernel addresses the block with 32-bit offsets from one descriptor per stream: every
+        // tile row of it must lie below 2 GiB
+        const bool small = tiles_m * tile_m * view_row_bytes < (uint64_t{1} << 31);
+        const bool fits = !part && !a2a && p.dest_group == 0 && small && ag::copy_ticket_supported(vec, W, tvpt, g);
         if (opt.tile_order == AG_ORDER_TICKETS) {
             if (!fits)
                 return fail(AG_ERR_UNSUPPORTED, "no ticket-order kernel for this call (%d-byte vectors, %d per thread, "
-                            "destination group %d)", vec, tvpt, p.dest_group);
+                            "destination group %d, %s 2 GiB of tile rows)", vec, tvpt, p.dest_group,
+                            small ? "under" : "not under");
             ticket = g;
         } else if (opt.tile_order == AG_ORDER_AUTO && fits && total >= AG_TICKETS_MIN_TILES_PER_PROGRAM * programs) {
             ticket = g;
@@ -603,8 +607,13 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     p.variant = kind;
     p.tile_order = ticket ? AG_ORDER_TICKETS : AG_ORDER_STRIDE;
     p.tiles_per_ticket = ticket;
-    // with at least one program per CU, each program waits for a ticket's stores before the next one's
-    p.ticket_wait = (ticket && grid >= static_cast<uint64_t>(geom->num_cus)) ? 1 : 0;
+    // Wide launches take each ticket after the stores of the batch before it (the program's first wave
+    // waits for them, the others at the barrier that hands the ticket out).  Measured at W=8,
+    // 16384x8192 on 256 CUs, it pays from 192 programs with one 16-byte vector per thread and tile
+    // (360 against 383 us per call at 192 programs, 361 against 389 at 256; 391 against 377 at 128)
+    // and from 96 with two (fp32: 731 against 776 us at 128 programs, 771 against 780 at 96; 1058
+    // against 1007 at 64): from three quarters of the CUs' worth of vectors in flight.
+    p.ticket_wait = (ticket && grid * static_cast<uint64_t>(tvpt) * 4 >= 3 * static_cast<uint64_t>(geom->num_cus)) ? 1 : 0;
     *plan = p;
     return ok();
 }

@@ -44,7 +44,7 @@ struct CopyLaunch {
     int grid;          // workgroups
     int wide;          // 1: the store policy of launches on at least half the CUs (no destination groups)
     int ticket;        // tiles per ticket of the ticket order (0: grid-stride order)
-    int drain;         // ticket order: wait for each ticket's stores before the next ticket's (needs wide)
+    int drain;         // ticket order: take each ticket after the stores of the batch before it
 };
 
 // Whether the launcher has a kernel for (kind, vec, dests, group, vpt, schedule) (host-only).

@@ -96,8 +96,9 @@ typedef struct ag_plan {
     int32_t schedule;            /* copy kernels: ag_schedule_t of the launch */
     int32_t tile_order;          /* copy kernels: ag_tile_order_t applied (AG_ORDER_STRIDE or AG_ORDER_TICKETS) */
     int32_t tiles_per_ticket;    /* copy kernels with AG_ORDER_TICKETS: consecutive tiles per ticket (else 0) */
-    int32_t ticket_wait;         /* AG_ORDER_TICKETS on at least one program per CU: 1 when each program waits
-                                    for a ticket's stores to complete before the next ticket's stores */
+    int32_t ticket_wait;         /* AG_ORDER_TICKETS on wide launches: 1 when each program takes a ticket only
+                                    after the stores of the batch before it have completed (its first wave
+                                    waits for them; the others wait at the barrier that hands it out) */
     int32_t reserved_plan;       /* 0 */
 } ag_plan_t;
 
@@ -116,9 +117,11 @@ typedef enum ag_tile_order {
     AG_ORDER_TICKETS = 2   /* programs take G consecutive tiles at a time from a device counter of the
                               calling rank, in increasing tile order (G = 4 at 256 or more programs, 8 at
                               128 or more, 16 below; 8 at most for two vectors per thread); 16-byte
-                              vectors, one or two per thread and tile, no destination groups.  With at
-                              least one program per CU, each program waits for a ticket's stores to
-                              complete before it stores the next ticket (plan.ticket_wait) */
+                              vectors, one or two per thread and tile, no destination groups, every
+                              tile row of the block below 2 GiB.  When programs x vectors per thread
+                              reach three quarters of the CU count, each program takes a ticket only
+                              after the stores of the batch before it have completed
+                              (plan.ticket_wait) */
 } ag_tile_order_t;
 
 /* Options of ag_all_gather_ex and ag_all_to_all_ex; all-zero (or a NULL pointer) is the plain call. */

@@ -465,13 +465,31 @@ def _big_geom(e=2, **kw):
     return geom(bytes_per_rank=8 * 16384 * 8192 * e + MiB, **kw)
 
 
-@pytest.mark.parametrize("progs,ticket,wait", [(256, 4, 1), (0, 4, 1), (512, 4, 1), (128, 8, 0), (64, 16, 0)])
+@pytest.mark.parametrize("progs,ticket,wait", [(256, 4, 1), (0, 4, 1), (512, 4, 1), (192, 8, 1), (191, 8, 0),
+                                                (128, 8, 0), (64, 16, 0)])
 def test_plan_tickets_for_long_calls(progs, ticket, wait):
     p = plan(g=_big_geom(), progs=progs, **BIG)
     assert p.tile_order == ag.AG_ORDER_TICKETS and p.tiles_per_ticket == ticket
     assert p.threads == 256 and p.n_programs == (progs or 256)
     assert p.total_tiles == 2048 * 32 and p.vectors_per_thread == 1
-    assert p.ticket_wait == wait               # one program per CU or more: a wait after every ticket
+    assert p.ticket_wait == wait               # from three quarters of the CUs (192 of 256): drained tickets
+
+
+@pytest.mark.parametrize("progs,wait", [(256, 1), (128, 1), (96, 1), (95, 0), (64, 0)])
+def test_plan_ticket_wait_with_two_vectors_per_thread(progs, wait):
+    p = plan(g=_big_geom(e=4), dtype="f32", progs=progs, **BIG)   # 8x256 fp32: two 16-byte vectors
+    assert p.vectors_per_thread == 2 and p.tile_order == ag.AG_ORDER_TICKETS
+    assert p.ticket_wait == wait               # programs x vectors from three quarters of the CUs
+
+
+def test_plan_no_tickets_past_2gib_of_tile_rows():
+    # 16384 x 32768 fp32 per rank: 2 GiB of input, beyond the ticket kernel's 32-bit tile offsets
+    g = geom(bytes_per_rank=8 * 16384 * 32768 * 4 + MiB)
+    p = plan(g=g, dtype="f32", progs=256, M=16384, N=32768)
+    assert p.tile_order == ag.AG_ORDER_STRIDE
+    with pytest.raises(ag.AgError) as exc:
+        ag.plan_all_gather_ex(g, 8, 0, 1, INPUT, 0, 16384, 32768, "f32", 0, 0, 256, tile_order="tickets")
+    assert exc.value.status == ag.AG_ERR_UNSUPPORTED
 
 
 def test_plan_tickets_two_vectors_per_thread_at_most_eight():

@@ -155,10 +155,11 @@ def test_ticket_order_in_place_and_random_bit_patterns():
         th.close()
 
 
-@pytest.mark.parametrize("dtype,programs", [("f16", 256), ("bf16", 300), ("f32", 256), ("f16", 128)])
+@pytest.mark.parametrize("dtype,programs", [("f16", 256), ("bf16", 300), ("f32", 256), ("f16", 128), ("f32", 96),
+                                            ("f32", 64), ("f16", 192)])
 def test_ticket_order_with_and_without_the_wait_after_each_ticket(dtype, programs):
-    """Enough tiles for a full-chip launch: at 256 programs or more each program waits for a ticket's
-    stores before the next ticket's (plan.ticket_wait), below it does not; same bytes either way."""
+    """Wide launches take each ticket after the stores of the batch before it (plan.ticket_wait), narrower
+    ones before; same bytes either way."""
     require_gpu()
     W, M, N = 4, 2048, 2048
     e = E[dtype]
@@ -169,7 +170,9 @@ def test_ticket_order_with_and_without_the_wait_after_each_ticket(dtype, program
         dev = [to_device(x) for x in ins]
         p = ag.plan_all_gather_ex(th.view(2).geometry(), W, 2, 1, dev[0], 256, M, N, dtype, 8, 256, programs,
                                   tile_order="tickets")
-        assert p.ticket_wait == (1 if programs >= th.view(2).geometry().num_cus else 0)
+        cus = th.view(2).geometry().num_cus
+        assert p.ticket_wait == (1 if 4 * min(programs, -(-p.total_tiles // p.tiles_per_ticket)) * p.vectors_per_thread
+                                 >= 3 * cus else 0)
         log(f"tickets {dtype} W={W} {M}x{N} programs={programs}: wait={p.ticket_wait} G={p.tiles_per_ticket}")
         before = th.host()
         _run(th, dev, W, 2, 1, 256, M, N, dtype, (8, 256), programs)
