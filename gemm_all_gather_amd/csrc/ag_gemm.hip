@@ -280,10 +280,11 @@ struct Stage {
         const uint32_t row = x / RB;
         return row * ld2 + ((x - row * RB) ^ (((row >> 3) & 1u) << 5));
     }
-    // The descriptor of N-contiguous stage kt starts at its first row: the
-    // buffer range check covers the VGPR and immediate offsets but not the
-    // SGPR one, so the stage offset goes into the base, and the columns past N
-    // of the last row of B read as zero instead of past the end of B.
+    // The descriptor of N-contiguous stage kt starts at its first row and
+    // ends at the end of B: the stage offset goes into the base and the
+    // extent, not into the SGPR offset, so the range check sees each lane's
+    // whole offset from the stage and the columns past N of the last row of B
+    // read as zero instead of past the end of B.
     static __device__ __forceinline__ __amdgpu_buffer_rsrc_t bt_rsrc(uint64_t base, uint64_t records, int kt,
                                                                      uint32_t ld2)
     {

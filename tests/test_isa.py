@@ -207,15 +207,17 @@ def test_ticket_kernel_hoists_bases_and_never_drains_before_a_store(asm, w, vpt,
     stores = [i for i, ln in enumerate(body) if ln.startswith("buffer_store")]
     assert len(loads) == 2 * G * VPT and len(stores) == 2 * G * W * VPT    # two batches per unrolled trip
     per_batch = G * W * VPT
-    for k, i in enumerate(stores):
-        prev = stores[k - 1] if k else 0
-        drains = [ln for ln in body[prev:i] if ln.startswith("s_waitcnt") and "vmcnt(0)" in ln]
-        if k % per_batch:                      # inside one ticket's run of stores: never
-            assert not drains, body[prev:i]
-        elif k and drain == "0":               # between tickets: only the draining variant waits
-            assert not drains, body[prev:i]
-        elif k and drain == "1":
-            assert len(drains) == 1, body[prev:i]
+    drains = [i for i, ln in enumerate(body) if ln.startswith("s_waitcnt") and "vmcnt(0)" in ln]
+    if drain == "0":                           # no store of the loop is preceded by a full drain
+        assert not [i for i in drains if i < stores[-1]], [body[i] for i in drains]
+    else:
+        # one drain per ticket, each the wait for the ticket's atomic, and between two drains (the loop
+        # body read cyclically, as blocks laid out ahead of the latch run after it) exactly one batch
+        # of stores, none of them behind a drain of its own
+        assert len(drains) == 2, [body[i] for i in drains]
+        assert all(any(ln.startswith("global_atomic_inc") for ln in body[i - 3:i]) for i in drains)
+        between = sum(drains[0] < i < drains[1] for i in stores)
+        assert between == per_batch and len(stores) - between == per_batch, (between, len(stores))
     assert not _sign_extended_lane_reads(lines)
     assert _meta(asm["ag_copy.hip"], sym)["scratch"] == 0
 
