@@ -437,7 +437,8 @@ def test_report_registers(asm, capsys):
     assert rows
     # the instantiations the benchmark workloads run, then a summary over all of them
     bench = [r"ag_copy_ticket_kernelILi16ELi8ELi1ELi4ELb1ELb1E", r"ag_copy_ticket_kernelILi16ELi8ELi1ELi8ELb1ELb0E",
-             r"ag_copy_ticket_kernelILi16ELi8ELi1ELi16ELb0ELb0E", r"ag_copy_ticket_kernelILi16ELi8ELi2ELi8ELb1ELb0E",
+             r"ag_copy_ticket_kernelILi16ELi8ELi1ELi16ELb0ELb0E", r"ag_copy_ticket_kernelILi16ELi8ELi2ELi4ELb1ELb1E",
+             r"ag_copy_ticket_kernelILi16ELi8ELi2ELi8ELb1ELb1E", r"ag_copy_ticket_kernelILi16ELi8ELi2ELi8ELb0ELb0E",
              r"ag_copy_kernelILi16ELi8ELi1ELi0ELb0ELb1E", r"ag_copy_kernelILi16ELi8ELi1ELi0ELb0ELb0E",
              r"ag_copy_kernelILi16ELi8ELi2ELi0ELb0ELb1E",
              r"ag_copy_kernelILi16ELi8ELi1ELi1ELb0ELb0E", r"ag_copy_kernelILi16ELi8ELi1ELi2ELb0ELb0E",
