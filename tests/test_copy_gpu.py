@@ -389,3 +389,43 @@ def test_full_size_w8_16384x8192(dtype):
 
 def test_full_size_strided_group_16384x8192():
     _full_size("f16", 4, 1, 2, 16384, 8192, [256], seed=11)
+
+
+# ---------------------------------------------------------------------------
+# maximum sizes: blocks on both sides of the ticket kernel's 2 GiB limit, and one past 4 GiB
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,order", [(32760, ag.AG_ORDER_TICKETS), (32776, ag.AG_ORDER_STRIDE),
+                                     (65544, ag.AG_ORDER_STRIDE)])
+def test_max_size_blocks(M, order):
+    """W=2, rows of 64 KiB (N=32768 fp16): tile rows just under 2 GiB per rank (ticket order, 32-bit tile
+    offsets), just over (grid stride), and a block past 4 GiB (64-bit tile offsets, descriptor extents
+    clamped below 2 GiB).  Both regions' outputs and guards are compared with the oracle's gathered block
+    on the device."""
+    require_gpu()
+    W, N, dtype = 2, 32768, "f16"
+    blk = M * N * 2
+    guard = 1 << 20
+    S = W * blk + 2 * guard
+    log(f"max-size all_gather W={W} {M}x{N} {dtype}: {blk / 2 ** 30:.3f} GiB per rank; generating inputs")
+    ins = [gen.random_bit_patterns((M, N), 2, 70, M, j) for j in range(W)]
+    dev = [to_device(x) for x in ins]
+    expect = to_device(all_gather_expected_block(ins))
+    del ins
+    th = TorchHeap(W, S)
+    try:
+        p = ag.plan_all_gather_ex(th.view(0).geometry(), W, 0, 1, dev[0], guard, M, N, dtype, 0, 0, 256)
+        assert p.tile_order == order
+        log(f"  tile order {p.tile_order}, {p.total_tiles} tiles, {p.n_programs} programs: running")
+        run_all_gather(th, dev, W, 0, 1, guard, M, N, dtype, 0, 0, 256)
+        torch.cuda.synchronize()
+        sentinel = torch.tensor([np.int16(np.uint16(gen.SENTINEL16).view(np.int16))], device="cuda")
+        for r in range(W):
+            reg = th.region(r)
+            assert torch.equal(reg[guard:guard + W * blk], expect), f"region {r} output differs"
+            assert torch.all(reg[:guard].view(torch.int16) == sentinel), f"region {r} front guard"
+            assert torch.all(reg[guard + W * blk:].view(torch.int16) == sentinel), f"region {r} back guard"
+    finally:
+        th.close()
+        del dev, expect
+        torch.cuda.empty_cache()
