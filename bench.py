@@ -48,9 +48,38 @@ FU_W, FU_N, FU_K, FU_DTYPE = 8, 3584, 8192, "f16"
 FU_M = 16384
 
 
+def _code_text(src: str) -> str:
+    """C++ source with its comments removed and whitespace collapsed: what the compiler sees of it.
+
+    String and character literals are kept as written (a // inside one is not a comment).
+    """
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def _src_hash(name: str) -> str:
-    with open(os.path.join(ROOT, "gemm_all_gather_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source's code (comments and layout excluded): a counter summary recorded on one
+    version of the code stays valid across comment edits and goes stale with any change to the code."""
+    with open(os.path.join(ROOT, "gemm_all_gather_amd", "csrc", name), encoding="utf-8") as f:
+        return hashlib.sha256(_code_text(f.read()).encode()).hexdigest()[:16]
 
 
 def _traffic(summary: str, source: str, per_launch_alg: float):

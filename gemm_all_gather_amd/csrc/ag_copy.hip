@@ -315,7 +315,8 @@ __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
 //
 // DRAIN false: the next ticket is taken before the stores of the batch in
 // hand, so waiting for it never waits for those stores.
-// DRAIN true (launches of at least one program per CU): the ticket is taken
+// DRAIN true (wide launches: programs x vectors per thread from three
+// quarters of the CU count, as the planner decides): the ticket is taken
 // after the batch's stores; thread 0 needs its value, so wave 0 waits for
 // everything it has issued, and the barrier that hands the ticket out holds
 // the other waves until then.  The next batch's loads go out right after, in
@@ -700,8 +701,8 @@ CopyFn pick_a2a_world(int w, int vpt, bool wide)
 
 // ---- ticket-order all-gather instantiations: 16-byte vectors, W = 1..8, one or two vectors per
 // thread per tile, 4, 8 or 16 tiles per ticket
-// (WIDE, DRAIN): (false, false) below half the CUs, (true, false) from half, (true, true) from one
-// program per CU
+// (WIDE, DRAIN): WIDE from half the CUs; DRAIN from three quarters of the CUs' worth of vectors
+// (programs x vectors per thread), with either store policy
 template <int W, int VPT, int G>
 CopyFn pick_ticket_policy(bool wide, bool drain)
 {
