@@ -99,6 +99,7 @@ _SIGNATURES = {
     "ag_heap_geometry": [_vp, ctypes.POINTER(Geometry)],
     "ag_heap_info": [_vp, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                      ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_void_p)],
+    "ag_heap_clear_tickets": [_vp, _vp],
     "ag_all_gather": [_vp, _c_int, _c_int, _c_int, _vp, _c_size, _c_i64, _c_i64, _c_int, _c_int, _c_int,
                       _c_int, _vp],
     "ag_plan_all_gather": [ctypes.POINTER(Geometry), _c_int, _c_int, _c_int, _c_u64, _c_size, _c_i64, _c_i64,
@@ -260,6 +261,10 @@ class Heap:
         _check(lib().ag_heap_info(self.handle, ctypes.byref(n), ctypes.byref(r), ctypes.byref(s), ctypes.byref(t)),
                "ag_heap_info")
         return {"n_ranks": n.value, "rank": r.value, "bytes_per_rank": s.value, "base_table": t.value or 0}
+
+    def clear_tickets(self, stream=None) -> None:
+        """ag_heap_clear_tickets: zero every rank's tile counters on stream."""
+        _check(lib().ag_heap_clear_tickets(self.handle, _stream(stream)), "ag_heap_clear_tickets")
 
 
 def plan_all_gather(geom: Geometry, W, rank_start, rank_stride, input_addr, out_offset, M_local, N, dtype,

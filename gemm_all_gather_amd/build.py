@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libag.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["ag_host.cpp", "ag_copy.hip", "ag_gemm.hip"]
+SOURCES = ["ag_host.cpp", "ag_copy.hip", "ag_gemm.hip", "ag_util.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -387,6 +387,18 @@ ag_status_t ag_heap_info(const ag_heap_t* heap, int* n_ranks, int* rank, size_t*
     return ok();
 }
 
+ag_status_t ag_heap_clear_tickets(const ag_heap_t* heap, void* stream)
+{
+    if (!heap) return fail(AG_ERR_INVALID_ARG, "heap is NULL");
+    ag_status_t s = check_device(heap);
+    if (s != AG_OK) return s;
+    const HeapCore& c = *heap->core;
+    const hipError_t e = ag::clear_counters(c.tickets, static_cast<uint32_t>(c.n_ranks) * (kTicketBytes / sizeof(uint32_t)),
+                                            static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(e, "clear_counters");
+    return ok();
+}
+
 // ---------------------------------------------------------------------------
 // all-gather (default, grouped, partitioned) and all-to-all: one planner
 // ---------------------------------------------------------------------------

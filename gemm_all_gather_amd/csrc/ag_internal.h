@@ -58,6 +58,8 @@ hipError_t launch_copy(const CopyLaunch& l, hipStream_t stream);
 // counter of a rank, after enqueueing on stream a small kernel that zeroes it.
 constexpr int kNoAllocMaxRanks = 64;
 hipError_t noalloc_tickets(int rank, hipStream_t stream, uint32_t** out);
+// Zeroes words [0, words) of a heap's tile counters with a kernel on stream (no memset: capturable).
+hipError_t clear_counters(uint32_t* counters, uint32_t words, hipStream_t stream);
 
 // Arguments of the fused GEMM + multi-destination store kernel.
 struct GemmKernelArgs {

@@ -179,6 +179,13 @@ ag_status_t ag_heap_alloc(ag_heap_t* heap, size_t bytes, size_t align, size_t* o
 /* Forget every allocation (offsets restart at 0). */
 ag_status_t ag_heap_reset(ag_heap_t* heap);
 
+/* Zero every rank's tile counters (the ticket order's; see ag_all_gather) with a small kernel on stream
+ * (hipStream_t; no memset, so the call can be captured in a graph).  The counters are zero between calls
+ * and need no clearing in correct use; this restores them after calls of one rank overlapped in time,
+ * which the all-gather does not allow and which can leave a counter non-zero for the rank's later calls.
+ * Stream-ordered; no call of this heap may run concurrently with it. */
+ag_status_t ag_heap_clear_tickets(const ag_heap_t* heap, void* stream);
+
 /* Device address of offset in region rank.  offset <= bytes_per_rank. */
 ag_status_t ag_heap_rank_ptr(const ag_heap_t* heap, int rank, size_t offset, void** dev_ptr);
 
@@ -234,7 +241,9 @@ ag_status_t ag_heap_info(const ag_heap_t* heap, int* n_ranks, int* rank, size_t*
  * concurrently on different streams.  Calls for the same rank must not
  * overlap in time (order them on one stream): a call in ticket order
  * (AG_ORDER_TICKETS, the library's choice for long calls) takes its tiles
- * from a counter the heap keeps for each rank, zero between calls.
+ * from a counter the heap keeps for each rank, zero between calls; calls of
+ * one rank that overlap give undefined output and may leave the counter
+ * non-zero for that rank's later calls (ag_heap_clear_tickets restores it).
  * M_local = 0 is a no-op.  input must not overlap any member's output
  * block, except that it may be exactly this rank's own rows in its own
  * region (in-place).

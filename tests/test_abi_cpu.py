@@ -252,6 +252,12 @@ def test_heap_info_rejects_a_null_handle():
     assert (n.value, r.value, s.value, t.value) == (7, 7, 7, 7)
 
 
+def test_heap_clear_tickets_rejects_a_null_handle():
+    l = ag.lib()
+    assert l.ag_heap_clear_tickets(None, None) == ag.AG_ERR_INVALID_ARG
+    assert "heap" in l.ag_last_error_message().decode()
+
+
 def test_heap_argument_validation_without_device():
     assert status_of(ag.Heap.create, 0, MiB)[0] == ag.AG_ERR_INVALID_ARG
     assert status_of(ag.Heap.create, 2, 0)[0] == ag.AG_ERR_INVALID_ARG

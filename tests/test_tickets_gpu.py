@@ -179,3 +179,47 @@ def test_ticket_order_with_and_without_the_wait_after_each_ticket(dtype, program
         _check(th, before, ins, S, 2, 1, 256)
     finally:
         th.close()
+
+
+def test_stale_counter_from_overlapping_calls_and_its_clearing():
+    """A counter left non-zero (what calls of one rank overlapping in time can leave, planted here from the
+    host) makes that rank's next ticket-order call skip tiles; ag_heap_clear_tickets restores it.  Every
+    kernel still ends normally: tickets past the last tile only end a program's loop."""
+    require_gpu()
+    W, M, N, dtype = 2, 512, 4096, "f16"
+    S = ((W * M * N * 2 + 4096) // 256 + 1) * 256
+    th = TorchHeap(2, S)
+    try:
+        ins = [gen.uniform_pm1((M, N), dtype, 66, j) for j in range(W)]
+        dev = [to_device(x) for x in ins]
+        info = th.heap.info()
+        start = info["base_table"] + -(-8 * info["n_ranks"] // 256) * 256
+
+        class _C:
+            __cuda_array_interface__ = {"shape": (info["n_ranks"] * 16,), "typestr": "<u4", "data": (start, False),
+                                        "version": 3, "strides": None}
+
+        counters = torch.as_tensor(_C(), device="cuda")
+        counters[0] = 100000          # rank 0's ticket counter, past every ticket of the call
+        counters[1] = 7               # and its finished-programs count
+        torch.cuda.synchronize()
+        before = th.host()
+        log("tickets: stale counter planted on rank 0")
+        _run(th, dev, W, 0, 1, 0, M, N, dtype, (8, 256), 4)
+        got = th.host()
+        want = all_gather_oracle(before, S, ins, 0, 1, 0)
+        blk = M * N * 2
+        # rank 0's rows were not stored anywhere; rank 1's were
+        for r in range(W):
+            assert np.array_equal(got[r * S:r * S + blk], before[r * S:r * S + blk]), "stale counter still copied"
+            assert np.array_equal(got[r * S + blk:r * S + 2 * blk], want[r * S + blk:r * S + 2 * blk])
+        th.heap.clear_tickets()
+        assert not _counters(th).any()
+        th.fill(gen.SENTINEL16)
+        torch.cuda.synchronize()
+        before = th.host()
+        log("tickets: after ag_heap_clear_tickets")
+        _run(th, dev, W, 0, 1, 0, M, N, dtype, (8, 256), 4)
+        _check(th, before, ins, S, 0, 1, 0)
+    finally:
+        th.close()
