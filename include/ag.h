@@ -96,9 +96,10 @@ typedef struct ag_plan {
     int32_t schedule;            /* copy kernels: ag_schedule_t of the launch */
     int32_t tile_order;          /* copy kernels: ag_tile_order_t applied (AG_ORDER_STRIDE or AG_ORDER_TICKETS) */
     int32_t tiles_per_ticket;    /* copy kernels with AG_ORDER_TICKETS: consecutive tiles per ticket (else 0) */
-    int32_t ticket_wait;         /* AG_ORDER_TICKETS on wide launches: 1 when each program takes a ticket only
-                                    after the stores of the batch before it have completed (its first wave
-                                    waits for them; the others wait at the barrier that hands it out) */
+    int32_t ticket_wait;         /* AG_ORDER_TICKETS on wide launches: 1 when each program takes its next
+                                    ticket after the stores of the batch in hand (its first wave waits for
+                                    its own stores to complete, and the barrier that hands the ticket out
+                                    holds the other waves until then), 0 when it takes it before them */
     int32_t reserved_plan;       /* 0 */
 } ag_plan_t;
 
@@ -119,9 +120,8 @@ typedef enum ag_tile_order {
                               128 or more, 16 below; 8 at most for two vectors per thread); 16-byte
                               vectors, one or two per thread and tile, no destination groups, every
                               tile row of the block below 2 GiB.  When programs x vectors per thread
-                              reach three quarters of the CU count, each program takes a ticket only
-                              after the stores of the batch before it have completed
-                              (plan.ticket_wait) */
+                              reach three quarters of the CU count, each program takes its next ticket
+                              after the stores of the batch in hand (plan.ticket_wait) */
 } ag_tile_order_t;
 
 /* Options of ag_all_gather_ex and ag_all_to_all_ex; all-zero (or a NULL pointer) is the plain call. */
