@@ -363,22 +363,23 @@ def _all_to_all(sub, stream, timed):
 
 
 def _context_fused(args, stream, timed, views, fu_off):
-    """The fused workload at M_local 1024 (fp16), at M_local 16384 in bf16, at M_local 16384 in fp16 with the
-    pages' 256x256 output tile, and at M_local 16384 in fp16 with B stored N-contiguous (a row-major K x N
-    matrix), W=8, timed like the headline."""
+    """The fused workload at M_local 1024 and 4096 (fp16; with 16384, the pages' three fused rows), at M_local
+    16384 in bf16, at M_local 16384 in fp16 with the pages' 256x256 output tile, and at M_local 16384 in fp16
+    with B stored N-contiguous (a row-major K x N matrix), W=8, timed like the headline."""
     import torch
     from gemm_all_gather_amd import binding as ag
 
     res = {}
     region = views[0].geometry().bytes_per_rank
     for name, M, dtype, layout, tile in (("M1024_f16", 1024, "f16", "k", (0, 0, 0)),
+                                         ("M4096_f16", 4096, "f16", "k", (0, 0, 0)),
                                          ("M16384_bf16", 16384, "bf16", "k", (0, 0, 0)),
                                          ("M16384_f16_tile_256x256x64", 16384, "f16", "k", (256, 256, 64)),
                                          ("M16384_f16_B_row_major_KxN", 16384, "f16", "n", (0, 0, 0))):
         sub = argparse.Namespace(**vars(args))
-        if M * FU_N * FU_K < (1 << 36):
-            # short calls (~75 us): the headline's warm-up steps, so the clocks settle after the workloads
-            # before (2 steps, about 1 ms, measured 88-93 us per call against 74.6 with 50)
+        if M * FU_N * FU_K < (1 << 38):
+            # short calls (75-220 us): the headline's warm-up steps, so the clocks settle after the workloads
+            # before (2 steps, about 1 ms, measured 88-93 us per call against 74.6 with 50 at M_local 1024)
             sub.steps, sub.warmup = max(20, args.steps // 5), args.warmup
         else:
             sub.steps, sub.warmup = max(5, args.steps // 10), 2
@@ -449,7 +450,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--fused-m", type=int, default=FU_M, help="M_local of the fused workload (16384 or 1024)")
+    ap.add_argument("--fused-m", type=int, default=FU_M, help="M_local of the fused workload (16384, 4096 or 1024)")
     ap.add_argument("--only", choices=["all", "copy", "fused", "a2a"], default="all",
                     help="restrict the timed step to one kernel (profiling runs); a2a times the all-to-all "
                          "context workload alone")

@@ -275,10 +275,19 @@ def test_full_size_m1024_fp16_every_element():
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_full_size_m16384(dtype, tile):
     """M_local 16384: the four corners and one interior entry of every output tile of every rank."""
+    _full_size_sampled(16384, dtype, tile, 41)
+
+
+def test_full_size_m4096_fp16():
+    """M_local 4096 (the pages' middle fused row: 256 tiles of 256x224, one per CU), sampled per tile."""
+    _full_size_sampled(4096, "f16", (0, 0, 0), 42)
+
+
+def _full_size_sampled(M, dtype, tile, seed):
     require_gpu()
-    M, N, K, W = 16384, 3584, 8192, 8
+    N, K, W = 3584, 8192, 8
     log(f"full-size fused W=8 M_local={M} N={N} K={K} {dtype} tile={tile}: generating inputs")
-    a, b = _inputs(M, N, K, dtype, 41)
+    a, b = _inputs(M, N, K, dtype, seed)
     a_dev = [to_device(x) for x in a]
     b_dev = to_device(b)
     blk = M * N * 2
@@ -293,7 +302,7 @@ def test_full_size_m16384(dtype, tile):
         torch.cuda.synchronize()
         ref_region = _full_size_heap(th, W, blk, guard)
         out = ref_region.cpu().numpy().view(np.uint16).reshape(W * M, N)
-        rng = np.random.default_rng([41, p.tile_m, p.tile_n])
+        rng = np.random.default_rng([seed, p.tile_m, p.tile_n])
         worst = 0.0
         for j in range(W):
             rows, cols = tile_samples(M, N, p.tile_m, p.tile_n, rng)
