@@ -643,10 +643,10 @@ __global__ __launch_bounds__(C::NT) void ag_gemm_kernel(GemmKernelArgs a)
 // full 128-byte line (measured 1.7x the L2 -> LDS throughput of 64-byte
 // rows), at the price of only two ring slots for the 256-row tiles.
 // Alternating loaders measured 5-7% faster at 256 x 224 (915 -> 850 us per
-// W=8 call at M_local 16384); the 256 x 256 tile keeps the loads spread over
-// all waves and double-buffered fragments.
+// W=8 call at M_local 16384) and 5-7% at 256 x 256 (928 -> 879 us in fp16,
+// 900 -> 840 in bf16, 254 -> 206 VGPRs with single-buffered fragments).
 #ifndef AG_GEMM_CFG_256x256
-#define AG_GEMM_CFG_256x256 256, 256, AG_GEMM_WGM, 2, 64, 2, false
+#define AG_GEMM_CFG_256x256 256, 256, AG_GEMM_WGM, 2, 64, 2, true
 #endif
 #ifndef AG_GEMM_CFG_256x224
 #define AG_GEMM_CFG_256x224 256, 224, AG_GEMM_WGM, 2, 64, 2, true
