@@ -195,16 +195,14 @@ ag_status_t check_group(const ag_heap_geometry_t* geom, int W, int rank_start, i
 #ifndef AG_COPY_NARROW_SLICES
 #define AG_COPY_NARROW_SLICES 4
 #endif
-// Ticket order (tile_order AG_ORDER_AUTO): tiles per ticket at >= 256, >= 128 and fewer programs, and
-// the tiles per program from which the library chooses tickets over the grid stride.
-#ifndef AG_TICKETS_G_WIDE
-#define AG_TICKETS_G_WIDE 4
-#endif
-#ifndef AG_TICKETS_G_MID
-#define AG_TICKETS_G_MID 8
-#endif
-#ifndef AG_TICKETS_G_NARROW
-#define AG_TICKETS_G_NARROW 16
+// Ticket order: tiles per ticket, the largest of 16, 8 and 4 whose tickets over all programs cover at
+// most AG_TICKETS_WINDOW_TILES tiles (at least 4).  Measured at W=8, 16384x8192, 8x256 tiles, us per
+// call with 4 / 8 / 16 tiles per ticket: 192 programs fp16 356 / 360 / -, fp32 700 / 728 / -;
+// 128 programs fp16 380 / 377 / 391, fp32 750 / 733 / -; 96 programs fp16 - / 399 / 406; 64 programs
+// fp16 - / 542 / 502.  And the tiles per program from which AG_ORDER_AUTO chooses tickets over the grid
+// stride.
+#ifndef AG_TICKETS_WINDOW_TILES
+#define AG_TICKETS_WINDOW_TILES 1024
 #endif
 #ifndef AG_TICKETS_MIN_TILES_PER_PROGRAM
 #define AG_TICKETS_MIN_TILES_PER_PROGRAM 64
@@ -573,7 +571,8 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     int ticket = 0;
     const int tvpt = static_cast<int>(tile_vecs / 256);   // 16-byte vectors per thread and tile (tickets)
     {
-        int g = programs >= 256 ? AG_TICKETS_G_WIDE : programs >= 128 ? AG_TICKETS_G_MID : AG_TICKETS_G_NARROW;
+        int g = 16;
+        while (g > 4 && static_cast<uint64_t>(g) * programs > AG_TICKETS_WINDOW_TILES) g /= 2;
         if (tvpt == 2 && g > 8) g = 8;
         // the ticket kernel addresses the block with 32-bit offsets from one descriptor per stream: every
         // tile row of it must lie below 2 GiB

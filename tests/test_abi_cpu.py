@@ -471,14 +471,17 @@ def _big_geom(e=2, **kw):
     return geom(bytes_per_rank=8 * 16384 * 8192 * e + MiB, **kw)
 
 
-@pytest.mark.parametrize("progs,ticket,wait", [(256, 4, 1), (0, 4, 1), (512, 4, 1), (192, 8, 1), (191, 8, 0),
-                                                (128, 8, 0), (64, 16, 0)])
+@pytest.mark.parametrize("progs,ticket,wait", [(256, 4, 1), (0, 4, 1), (512, 4, 1), (192, 4, 1), (191, 4, 0),
+                                                (129, 4, 0), (128, 8, 0), (96, 8, 0), (65, 8, 0), (64, 16, 0),
+                                                (32, 16, 0)])
 def test_plan_tickets_for_long_calls(progs, ticket, wait):
     p = plan(g=_big_geom(), progs=progs, **BIG)
     assert p.tile_order == ag.AG_ORDER_TICKETS and p.tiles_per_ticket == ticket
     assert p.threads == 256 and p.n_programs == (progs or 256)
     assert p.total_tiles == 2048 * 32 and p.vectors_per_thread == 1
     assert p.ticket_wait == wait               # from three quarters of the CUs (192 of 256): drained tickets
+    # tiles per ticket: the largest of 16, 8, 4 whose tickets over all programs span at most 1024 tiles
+    assert p.tiles_per_ticket * p.n_programs <= 1024 or p.tiles_per_ticket == 4
 
 
 @pytest.mark.parametrize("progs,wait", [(256, 1), (128, 1), (96, 1), (95, 0), (64, 0)])
