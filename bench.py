@@ -256,8 +256,8 @@ class _Workload:
 def _context(args, stream, timed, head):
     """Context measurements beside the headline (each job = the group members' calls, timed like it).
 
-    * the 16384x8192 all-gather at 64/128/256 programs in fp16, bf16 and fp32, in the library's tile order
-      (tickets at this size) and in the fixed grid-stride order;
+    * the 16384x8192 all-gather at 64/128/256 programs (and 192) in fp16, bf16 and fp32, in the library's
+      tile order (tickets at this size) and in the fixed grid-stride order;
     * its variants: destination groups 1/2/4 and the partitioned schedule at 64/128/256 programs;
     * the 1024x4096 all-gather at 64/128/256 programs (75 MB per call: partly held by the last-level
       cache, so its rate exceeds what HBM sustains for the larger shape);
@@ -281,7 +281,7 @@ def _context(args, stream, timed, head):
     for dt in ("f16", "bf16", "f32"):
         wl = head if dt == "f16" else _Workload(AG_M, AG_N, dt, seed=6)
         big[dt] = {}
-        for P in (64, 128, 256):
+        for P in (64, 128, 192, 256):   # the workload's 64/128/256 programs, and 192 between them
             gb, ms = rate(wl, tile=AG_TILE, programs=P)
             p = wl.plan(ag, AG_TILE, P)
             entry = {"GBs": gb, "frac": round(gb / HBM_PEAK_GBS, 4), "us_per_call": round(ms * 1e3 / wl.W, 2),
