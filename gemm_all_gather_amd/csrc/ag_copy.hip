@@ -700,7 +700,7 @@ CopyFn pick_a2a_world(int w, int vpt, bool wide)
 }
 
 // ---- ticket-order all-gather instantiations: 16-byte vectors, W = 1..8, one or two vectors per
-// thread per tile, 4, 8 or 16 tiles per ticket
+// thread per tile, 4, 8 or 16 tiles per ticket, and 3 (one vector) or 2 (two) for full-chip launches
 // (WIDE, DRAIN): WIDE from half the CUs; DRAIN from three quarters of the CUs' worth of vectors
 // (programs x vectors per thread), with either store policy
 template <int W, int VPT, int G>
@@ -714,6 +714,12 @@ template <int W, int VPT>
 CopyFn pick_ticket_g(int ticket, bool wide, bool drain)
 {
     switch (ticket) {
+    case 2:
+        if constexpr (VPT == 2) return pick_ticket_policy<W, VPT, 2>(wide, drain);
+        return nullptr;
+    case 3:
+        if constexpr (VPT == 1) return pick_ticket_policy<W, VPT, 3>(wide, drain);
+        return nullptr;
     case 4: return pick_ticket_policy<W, VPT, 4>(wide, drain);
     case 8: return pick_ticket_policy<W, VPT, 8>(wide, drain);
     case 16:

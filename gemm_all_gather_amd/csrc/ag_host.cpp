@@ -195,14 +195,23 @@ ag_status_t check_group(const ag_heap_geometry_t* geom, int W, int rank_start, i
 #ifndef AG_COPY_NARROW_SLICES
 #define AG_COPY_NARROW_SLICES 4
 #endif
-// Ticket order: tiles per ticket, the largest of 16, 8 and 4 whose tickets over all programs cover at
-// most AG_TICKETS_WINDOW_TILES tiles (at least 4).  Measured at W=8, 16384x8192, 8x256 tiles, us per
-// call with 4 / 8 / 16 tiles per ticket: 192 programs fp16 356 / 360 / -, fp32 700 / 728 / -;
-// 128 programs fp16 380 / 377 / 391, fp32 750 / 733 / -; 96 programs fp16 - / 399 / 406; 64 programs
-// fp16 - / 542 / 502.  And the tiles per program from which AG_ORDER_AUTO chooses tickets over the grid
-// stride.
+// Ticket order, tiles per ticket G.  Each ticket is one increment of the calling rank's counter, and
+// increments of one address retire about one per 12 ns: at W=2 and W=4, 16384x8192 fp16, 256 programs,
+// the call took the ticket count times that (W=2: 263 / 204 / 125 us per call with 3 / 4 / 8 tiles per
+// ticket; W=4: 266 / 207 / 203).  So a ticket must move at least AG_TICKETS_MIN_BYTES of HBM traffic (its
+// tiles read once and written W times).  Above that floor fewer tiles per ticket keep the tiles in flight
+// in a narrower window: a launch on fewer programs than CUs takes the largest of 16, 8 and 4 whose
+// tickets over all programs cover at most AG_TICKETS_WINDOW_TILES tiles, a launch with a program per CU
+// the smallest G the floor allows.  Measured at W=8, 16384x8192, 8x256 tiles, us per call with
+// 4 / 8 / 16 tiles per ticket: 192 programs fp16 356 / 360 / -, fp32 700 / 728 / -; 128 programs fp16
+// 380 / 377 / 391, fp32 750 / 733 / -; 96 programs fp16 - / 399 / 406; 64 programs fp16 - / 542 / 502;
+// 256 programs fp16 with 2 / 3 / 4: 390 / 357 / 362.  AG_TICKETS_MIN_TILES_PER_PROGRAM is the tiles per
+// program from which AG_ORDER_AUTO chooses tickets over the grid stride.
 #ifndef AG_TICKETS_WINDOW_TILES
 #define AG_TICKETS_WINDOW_TILES 1024
+#endif
+#ifndef AG_TICKETS_MIN_BYTES
+#define AG_TICKETS_MIN_BYTES (96u << 10)
 #endif
 #ifndef AG_TICKETS_MIN_TILES_PER_PROGRAM
 #define AG_TICKETS_MIN_TILES_PER_PROGRAM 64
@@ -571,11 +580,28 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     int ticket = 0;
     const int tvpt = static_cast<int>(tile_vecs / 256);   // 16-byte vectors per thread and tile (tickets)
     {
-        int g = 16;
-        while (g > 4 && static_cast<uint64_t>(g) * programs > AG_TICKETS_WINDOW_TILES) g /= 2;
-        if (tvpt == 2 && g > 8) g = 8;
-        // the ticket kernel addresses the block with 32-bit offsets from one descriptor per stream: every
-        // tile row of it must lie below 2 GiB
+        // tiles per ticket: the ticket kernels exist for 3, 4, 8 and 16 tiles with one vector per
+        // thread and 2, 4 and 8 with two
+        static constexpr int kSizesVpt1[] = {3, 4, 8, 16};
+        static constexpr int kSizesVpt2[] = {2, 4, 8};
+        const int* sizes = tvpt == 2 ? kSizesVpt2 : kSizesVpt1;
+        const int n_sizes = tvpt == 2 ? 3 : 4;
+        const uint64_t hbm_bytes_per_tile = tile_vecs * vec * (1 + static_cast<uint64_t>(W));
+        int g_floor = sizes[n_sizes - 1];
+        for (int i = 0; i < n_sizes; ++i) {
+            if (sizes[i] * hbm_bytes_per_tile >= AG_TICKETS_MIN_BYTES) {
+                g_floor = sizes[i];
+                break;
+            }
+        }
+        int g = sizes[0];
+        if (programs < static_cast<uint64_t>(geom->num_cus)) {
+            g = 16;
+            while (g > 4 && static_cast<uint64_t>(g) * programs > AG_TICKETS_WINDOW_TILES) g /= 2;
+            g = std::min(g, sizes[n_sizes - 1]);
+        }
+        g = std::max(g, g_floor);
+        // the ticket kernel's tile offsets are 32-bit: every tile row of the block must lie below 2 GiB
         const bool small = tiles_m * tile_m * view_row_bytes < (uint64_t{1} << 31);
         const bool fits = !part && !a2a && p.dest_group == 0 && small && ag::copy_ticket_supported(vec, W, tvpt, g);
         if (opt.tile_order == AG_ORDER_TICKETS) {

@@ -116,11 +116,13 @@ typedef enum ag_tile_order {
                               program where a ticket kernel exists, AG_ORDER_STRIDE otherwise */
     AG_ORDER_STRIDE = 1,   /* fixed grid stride: program p takes tiles p, p + P, p + 2P, ... */
     AG_ORDER_TICKETS = 2   /* programs take G consecutive tiles at a time from a device counter of the
-                              calling rank, in increasing tile order (G is the largest of 16, 8 and 4
-                              with G x programs <= 1024, and at least 4; 8 at most for two vectors per
-                              thread); 16-byte
-                              vectors, one or two per thread and tile, no destination groups, every
-                              tile row of the block below 2 GiB.  When programs x vectors per thread
+                              calling rank, in increasing tile order; 16-byte vectors, one or two per
+                              thread and tile, no destination groups, every tile row of the block below
+                              2 GiB.  G is one of 3, 4, 8, 16 (one vector per thread) or 2, 4, 8 (two):
+                              the smallest whose tiles, read once and written W times, move at least
+                              96 KiB of HBM traffic (the largest where none does), and on launches with
+                              fewer programs than CUs at least the largest of 16, 8 and 4 (within those
+                              sizes) with G x programs <= 1024.  When programs x vectors per thread
                               reach three quarters of the CU count, each program takes its next ticket
                               after the stores of the batch in hand (plan.ticket_wait) */
 } ag_tile_order_t;

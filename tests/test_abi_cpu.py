@@ -471,7 +471,7 @@ def _big_geom(e=2, **kw):
     return geom(bytes_per_rank=8 * 16384 * 8192 * e + MiB, **kw)
 
 
-@pytest.mark.parametrize("progs,ticket,wait", [(256, 4, 1), (0, 4, 1), (512, 4, 1), (192, 4, 1), (191, 4, 0),
+@pytest.mark.parametrize("progs,ticket,wait", [(256, 3, 1), (0, 3, 1), (512, 3, 1), (192, 4, 1), (191, 4, 0),
                                                 (129, 4, 0), (128, 8, 0), (96, 8, 0), (65, 8, 0), (64, 16, 0),
                                                 (32, 16, 0)])
 def test_plan_tickets_for_long_calls(progs, ticket, wait):
@@ -481,7 +481,25 @@ def test_plan_tickets_for_long_calls(progs, ticket, wait):
     assert p.total_tiles == 2048 * 32 and p.vectors_per_thread == 1
     assert p.ticket_wait == wait               # from three quarters of the CUs (192 of 256): drained tickets
     # tiles per ticket: the largest of 16, 8, 4 whose tickets over all programs span at most 1024 tiles
-    assert p.tiles_per_ticket * p.n_programs <= 1024 or p.tiles_per_ticket == 4
+    # (from one program per CU, 3: 12 KiB of 8x256 fp16 tiles, 108 KiB of HBM traffic per ticket at W=8)
+    assert p.tiles_per_ticket * p.n_programs <= 1024 or p.tiles_per_ticket <= 4
+
+
+# every ticket moves at least 96 KiB of HBM traffic (its tiles read once and written W times): one
+# counter hands out about one ticket per 12 ns, which bounds small-W calls with small tickets
+@pytest.mark.parametrize("W,start,stride,dtype,progs,ticket", [
+    (8, 0, 1, "f16", 256, 3), (7, 0, 1, "f16", 256, 3), (6, 0, 1, "f16", 256, 4), (5, 0, 1, "f16", 256, 4),
+    (4, 1, 2, "f16", 256, 8), (4, 0, 1, "f16", 192, 8), (3, 0, 1, "f16", 256, 8), (2, 0, 1, "f16", 256, 8),
+    (1, 0, 1, "f16", 256, 16), (1, 0, 1, "f16", 128, 16), (2, 0, 1, "f16", 64, 16),
+    (8, 0, 1, "f32", 256, 2), (4, 1, 2, "f32", 256, 4), (2, 0, 1, "f32", 256, 4), (1, 0, 1, "f32", 256, 8),
+    (4, 0, 1, "f32", 128, 8)])
+def test_plan_tiles_per_ticket_move_96_kib(W, start, stride, dtype, progs, ticket):
+    e = 4 if dtype == "f32" else 2
+    p = plan(g=_big_geom(e=e, rank=start), W=W, start=start, stride=stride, dtype=dtype, progs=progs, **BIG)
+    assert p.tile_order == ag.AG_ORDER_TICKETS and p.tiles_per_ticket == ticket
+    tile_bytes = 8 * 256 * e
+    # at least 96 KiB per ticket wherever a ticket kernel that large exists
+    assert ticket * tile_bytes * (1 + W) >= 96 << 10 or ticket == (8 if e == 4 else 16)
 
 
 @pytest.mark.parametrize("progs,wait", [(256, 1), (128, 1), (96, 1), (95, 0), (64, 0)])
@@ -519,7 +537,7 @@ def test_plan_short_calls_keep_the_grid_stride():
 
 def test_plan_ticket_grid_is_capped_by_tickets():
     p = ag.plan_all_gather_ex(geom(), 8, 0, 1, INPUT, 0, 64, 256, "f16", 8, 256, 256, tile_order="tickets")
-    assert p.total_tiles == 8 and p.tiles_per_ticket == 4 and p.n_programs == 2
+    assert p.total_tiles == 8 and p.tiles_per_ticket == 3 and p.n_programs == 3     # ceil(8 / 3) tickets
 
 
 @pytest.mark.parametrize("kw,status", [

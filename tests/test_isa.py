@@ -181,7 +181,8 @@ def test_all_to_all_kernel_hoists_bases_and_pipelines_tiles(asm, vec, w, vpt):
     assert _meta(asm["ag_copy.hip"], sym)["scratch"] == 0
 
 
-@pytest.mark.parametrize("w,vpt,g,wide,drain", [("8", "1", "4", "1", "1"), ("8", "1", "4", "1", "0"),
+@pytest.mark.parametrize("w,vpt,g,wide,drain", [("8", "1", "3", "1", "1"), ("8", "2", "2", "1", "1"),
+                                                ("8", "1", "4", "1", "1"), ("8", "1", "4", "1", "0"),
                                                 ("8", "1", "8", "1", "0"), ("8", "1", "16", "0", "0"),
                                                 ("8", "2", "8", "0", "0"), ("4", "1", "4", "1", "1"),
                                                 ("1", "2", "4", "1", "0")])
@@ -436,9 +437,11 @@ def test_report_registers(asm, capsys):
                 rows.append((sym, _meta(asm[src], sym)))
     assert rows
     # the instantiations the benchmark workloads run, then a summary over all of them
-    bench = [r"ag_copy_ticket_kernelILi16ELi8ELi1ELi4ELb1ELb1E", r"ag_copy_ticket_kernelILi16ELi8ELi1ELi8ELb1ELb0E",
-             r"ag_copy_ticket_kernelILi16ELi8ELi1ELi16ELb0ELb0E", r"ag_copy_ticket_kernelILi16ELi8ELi2ELi4ELb1ELb1E",
-             r"ag_copy_ticket_kernelILi16ELi8ELi2ELi8ELb1ELb1E", r"ag_copy_ticket_kernelILi16ELi8ELi2ELi8ELb0ELb0E",
+    bench = [r"ag_copy_ticket_kernelILi16ELi8ELi1ELi3ELb1ELb1E", r"ag_copy_ticket_kernelILi16ELi8ELi1ELi4ELb1ELb1E",
+             r"ag_copy_ticket_kernelILi16ELi8ELi1ELi8ELb1ELb0E",
+             r"ag_copy_ticket_kernelILi16ELi8ELi1ELi16ELb0ELb0E", r"ag_copy_ticket_kernelILi16ELi8ELi2ELi2ELb1ELb1E",
+             r"ag_copy_ticket_kernelILi16ELi8ELi2ELi4ELb1ELb1E", r"ag_copy_ticket_kernelILi16ELi8ELi2ELi8ELb1ELb1E",
+             r"ag_copy_ticket_kernelILi16ELi8ELi2ELi8ELb0ELb0E",
              r"ag_copy_kernelILi16ELi8ELi1ELi0ELb0ELb1E", r"ag_copy_kernelILi16ELi8ELi1ELi0ELb0ELb0E",
              r"ag_copy_kernelILi16ELi8ELi2ELi0ELb0ELb1E",
              r"ag_copy_kernelILi16ELi8ELi1ELi1ELb0ELb0E", r"ag_copy_kernelILi16ELi8ELi1ELi2ELb0ELb0E",

@@ -82,7 +82,7 @@ def test_ticket_order_sweep(W, start, stride, M, N):
         dev = [to_device(x) for x in ins]
         p = ag.plan_all_gather_ex(th.view(start).geometry(), W, start, stride, dev[0], off, M, N, dtype, *tile,
                                   programs, tile_order="tickets")
-        assert p.tile_order == ag.AG_ORDER_TICKETS and p.tiles_per_ticket in (4, 8, 16)
+        assert p.tile_order == ag.AG_ORDER_TICKETS and p.tiles_per_ticket in (2, 3, 4, 8, 16)
         before = th.host()
         _run(th, dev, W, start, stride, off, M, N, dtype, tile, programs)
         _check(th, before, ins, S, start, stride, off)
