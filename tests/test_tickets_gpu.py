@@ -90,6 +90,38 @@ def test_ticket_order_sweep(W, start, stride, M, N):
         th.close()
 
 
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_ticket_order_every_world_on_every_cu(W, dtype):
+    """A program per CU, 8x256 tiles: each W takes the tiles per ticket of its 96 KiB floor (3 to 16 with one
+    16-byte vector per thread, 2 to 8 with two) and the schedule that takes tickets after the stores."""
+    require_gpu()
+    e = E[dtype]
+    # 25 tile columns (the last one partial) and enough tiles that every program takes tickets: 3200 tiles
+    # up to W=4 (16 or 8 per ticket), 1600 from W=5 (at most 4 per ticket)
+    M, N = (1024 if W <= 4 else 512), 6152
+    start, stride = (0, 1) if W > 4 else (1, 2) if W > 1 else (1, 1)
+    S = ((W * M * N * e + 4096) // 256 + 1) * 256
+    th = TorchHeap(8, S)
+    try:
+        ins = [gen.uniform_pm1((M, N), dtype, 70 + W, j) for j in range(W)]
+        dev = [to_device(x) for x in ins]
+        cus = th.view(start).geometry().num_cus
+        p = ag.plan_all_gather_ex(th.view(start).geometry(), W, start, stride, dev[0], 0, M, N, dtype, 8, 256, cus,
+                                  tile_order="tickets")
+        tile_bytes = 8 * 256 * e
+        assert p.tile_order == ag.AG_ORDER_TICKETS
+        assert p.tiles_per_ticket * tile_bytes * (1 + W) >= 96 << 10 or p.tiles_per_ticket == (16 if e == 2 else 8)
+        assert p.n_programs >= 3 * cus // 4 and p.ticket_wait == 1
+        log(f"tickets on every CU: W={W} {dtype} G={p.tiles_per_ticket} wait={p.ticket_wait} "
+            f"programs={p.n_programs}")
+        before = th.host()
+        _run(th, dev, W, start, stride, 0, M, N, dtype, (8, 256), cus)
+        _check(th, before, ins, S, start, stride, 0)
+    finally:
+        th.close()
+
+
 def test_ticket_order_repeated_calls_and_counter_reset():
     """The same call again and again, then other ranks and shapes: the counters are zero between calls."""
     require_gpu()
