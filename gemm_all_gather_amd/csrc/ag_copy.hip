@@ -301,7 +301,10 @@ __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
 // stay dense (W=8, 16384x8192 fp16, 256 programs: 373 against 448 us per call
 // in a measured replica).  Each ticket is one relaxed device-scope atomic
 // increment by one thread, handed to the workgroup through LDS; the last
-// program to finish resets the counter, so it is zero at every launch.  Two
+// program to finish resets the counter, so it is zero at every launch.  One
+// counter serves about one increment per 12 ns, so the planner sizes G for
+// at least 96 KiB of HBM traffic per ticket where a kernel that large exists
+// (at W=4, 3 tiles of 8x256 fp16 per ticket made the call counter-bound).  Two
 // batches of G tiles live in registers: the next one loading while the one in
 // hand is stored.
 //
