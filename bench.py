@@ -333,7 +333,8 @@ def _all_to_all(sub, stream, timed):
     from gemm_all_gather_amd import binding as ag
 
     # all-to-all: each rank sends 8 chunks of 1024x4096 fp16 (64 MiB per rank); 8x512 tiles, two 16-byte
-    # vectors per thread (measured 5.3 TB/s against 5.0 for 8x256 at 256 programs)
+    # vectors per thread (22.9 us per call against 28.5 for 8x256 and 23.0-24.6 for larger tiles at 256
+    # programs)
     A2A_TILE = (8, 512)
     mc, n = SM_M, SM_N
     # inputs of W chunks; regions sized for the exchanged output (W chunks of M_chunk x N)

@@ -539,11 +539,9 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
         return v;
     };
     const uint64_t tile_row_bytes = static_cast<uint64_t>(tile_n) * e;
-    // the all-to-all's tile schedule holds W tiles per thread: <= 32 bytes of each
-    auto max_vpt_of = [&](int v) { return (a2a && !part) ? std::min(32 / v, kCopyMaxVpt) : kCopyMaxVpt; };
     auto tile_fits = [&](int v) {
         const uint64_t tv = static_cast<uint64_t>(tile_m) * tile_row_bytes / v;
-        return tv % 256 == 0 && tv / 256 <= static_cast<uint64_t>(max_vpt_of(v));
+        return tv % 256 == 0 && tv / 256 <= static_cast<uint64_t>(kCopyMaxVpt);
     };
     int vec = widest(row_bytes);
     uint64_t rows = static_cast<uint64_t>(M), cols = static_cast<uint64_t>(N);
@@ -558,10 +556,9 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     }
     const uint64_t view_row_bytes = cols * static_cast<uint64_t>(e);
     const uint64_t tile_vecs = static_cast<uint64_t>(tile_m) * tile_row_bytes / vec;
-    const int max_vpt = max_vpt_of(vec);
-    if (tile_vecs % 256 != 0 || tile_vecs / 256 > static_cast<uint64_t>(max_vpt))
+    if (tile_vecs % 256 != 0 || tile_vecs / 256 > static_cast<uint64_t>(kCopyMaxVpt))
         return fail(AG_ERR_UNSUPPORTED, "tile %dx%d holds %llu %d-byte vectors; 256 to %d are supported",
-                    tile_m, tile_n, static_cast<unsigned long long>(tile_vecs), vec, 256 * max_vpt);
+                    tile_m, tile_n, static_cast<unsigned long long>(tile_vecs), vec, 256 * kCopyMaxVpt);
     if (static_cast<uint64_t>(tile_m) * view_row_bytes >= (uint64_t{1} << 31))
         return fail(AG_ERR_UNSUPPORTED, "a tile spans 2 GiB or more of the input");
     if (p.dest_group > 0 && vec < 8)
@@ -571,6 +568,9 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     const uint64_t tiles_n = ceil_div(cols, tile_n);
     const uint64_t total = tiles_m * tiles_n;
     if (total >= (uint64_t{1} << 31)) return fail(AG_ERR_UNSUPPORTED, "more than 2^31 tiles");
+    // the all-to-all kernel walks the W chunks' tiles as one sequence
+    if (a2a && total * static_cast<uint64_t>(W) >= (uint64_t{1} << 31))
+        return fail(AG_ERR_UNSUPPORTED, "more than 2^31 tiles over the W chunks");
 
     const uint64_t programs = n_programs == 0 ? geom->num_cus : n_programs;
     // Tile order of the tile schedule.  Tickets (consecutive tiles handed out in increasing order
@@ -626,7 +626,8 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
         const uint64_t max_slices = 2 * programs < static_cast<uint64_t>(geom->num_cus) ? kCopyNarrowSlices
                                                                                      : static_cast<uint64_t>(kCopyMaxSlices);
         while (!a2a && slices < max_slices && programs * slices * 2 <= total) slices *= 2;
-        grid = std::min<uint64_t>(programs, ceil_div(total, slices));
+        // (the all-to-all walks W x total tiles: the block's tiles of each of the W chunks)
+        grid = std::min<uint64_t>(programs, a2a ? total * static_cast<uint64_t>(W) : ceil_div(total, slices));
     }
     if (grid >= (uint64_t{1} << 31)) return fail(AG_ERR_UNSUPPORTED, "n_programs too large");
     const int vpt = static_cast<int>(tile_vecs / 256);

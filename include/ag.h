@@ -339,12 +339,14 @@ ag_status_t ag_all_gather_noalloc(const ag_heap_t* heap, int W, int rank_start, 
  *               output inside every member region
  * After the call completes, rows [g*M_chunk, (g+1)*M_chunk) of member j's
  * output hold chunk j of this rank's input; no other byte of the slab
- * changes.  Every destination base is translated once before the tile loop;
- * for each tile the W chunks' tiles are loaded, then stored local region
- * first and the peers in rotated order.  Tiles as for ag_all_gather (0,0 =
- * 8x256), holding at most 32 bytes per thread of a 256-thread workgroup
- * (AG_ERR_UNSUPPORTED otherwise; 8x256 always fits).  M_chunk = 0 is a
- * no-op.  input must not overlap any member's output block.
+ * changes.  Every destination base is translated once before the tile loop.
+ * The W chunk copies are walked as one sequence of W x (tiles per chunk)
+ * tiles, destination by destination: the local region first, then the peers
+ * in rotated order; each tile is loaded once and stored once.  Tiles as for
+ * ag_all_gather (0,0 = 8x256): 1 to 8 vectors per thread of a 256-thread
+ * workgroup (AG_ERR_UNSUPPORTED otherwise; 8x256 always fits); W x tiles per
+ * chunk below 2^31.  M_chunk = 0 is a no-op.  input must not overlap any
+ * member's output block.
  * ------------------------------------------------------------------------ */
 ag_status_t ag_all_to_all(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
                           const void* input, size_t out_offset, int64_t M_chunk, int64_t N,
@@ -361,8 +363,7 @@ ag_status_t ag_plan_all_to_all(const ag_heap_geometry_t* geom, int W, int rank_s
  * applied to the exchange): program p owns destination i = p mod W of the
  * rotated order and copies chunk (g + i) mod W there, the programs of one
  * destination walking all tiles among themselves; every chunk is read once.
- * n_programs is rounded down to a multiple of W (at least W); tiles may
- * then hold up to 8 vectors per thread, as for ag_all_gather. */
+ * n_programs is rounded down to a multiple of W (at least W). */
 ag_status_t ag_all_to_all_ex(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
                              const void* input, size_t out_offset, int64_t M_chunk, int64_t N,
                              ag_dtype_t dtype, int tile_m, int tile_n, int n_programs,

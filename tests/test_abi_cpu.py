@@ -349,7 +349,7 @@ def test_plan_all_to_all_strided_group_and_zero_rows():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(tm=8, tn=512, dtype="f32"), ag.AG_ERR_UNSUPPORTED),     # 64 bytes per thread: at most 32
+    (dict(tm=32, tn=512, dtype="f32"), ag.AG_ERR_UNSUPPORTED),    # 16 vectors per thread: at most 8
     (dict(M=-1), ag.AG_ERR_INVALID_ARG),
     (dict(M=1 << 20), ag.AG_ERR_INVALID_ARG),                     # output block past the region
     (dict(inp=0), ag.AG_ERR_INVALID_ARG),
@@ -394,11 +394,14 @@ def test_plan_all_to_all_partitioned_programs(W, progs, grid):
     assert p.bytes_read == W * blk and p.bytes_written == W * blk    # every chunk read once
 
 
-def test_plan_all_to_all_partitioned_allows_more_vectors_per_thread():
-    # one tile in registers per program: 4 vectors of 16 bytes, beyond the tile schedule's 32 bytes of each chunk
-    assert status_of(plan_a2a_ex, tm=32, tn=256)[0] == ag.AG_ERR_UNSUPPORTED
-    p = plan_a2a_ex(tm=32, tn=256, sched="partitioned")
-    assert (p.vec_bytes, p.vectors_per_thread) == (16, 4)
+def test_plan_all_to_all_takes_up_to_eight_vectors_per_thread():
+    # both schedules hold one chunk tile per step in registers: up to 8 vectors of 16 bytes per thread
+    for sched in ("tiles", "partitioned"):
+        p = plan_a2a_ex(tm=32, tn=256, sched=sched)
+        assert (p.vec_bytes, p.vectors_per_thread) == (16, 4)
+        p = plan_a2a_ex(tm=64, tn=256, sched=sched)
+        assert (p.vec_bytes, p.vectors_per_thread) == (16, 8)
+        assert status_of(plan_a2a_ex, tm=128, tn=256, sched=sched)[0] == ag.AG_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -163,17 +163,23 @@ def test_grouped_copy_waits_once_per_destination_group(asm, w, g):
 
 @pytest.mark.parametrize("vec,w,vpt", [(16, 8, 1), (16, 8, 2), (16, 4, 1), (16, 2, 2), (8, 8, 4), (2, 3, 8)])
 def test_all_to_all_kernel_hoists_bases_and_pipelines_tiles(asm, vec, w, vpt):
+    """The W chunk copies as one sequence of tiles: one chunk tile loaded and stored per step, two steps
+    per unrolled trip, the next tile's load ahead of the current tile's stores, no drain before a store.
+    The table is read once before the loop; in the loop each stored tile reads its destination base from
+    the lanes that hold them (two readlanes with a scalar lane index), never from memory."""
     sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_a2a_kernelILi{vec}ELi{w}ELi{vpt}E")
     loops = _loops(lines)
     assert loops, "tile loop not found"
     h, b = _outermost(loops)
     body, prologue = lines[h:b + 1], lines[:h]
     assert not any(ln.startswith("s_load") for ln in body), "scalar load inside the tile loop"
+    assert not any(re.match(r"(global|flat)_load", ln) for ln in body), "table read inside the tile loop"
     assert sum(ln.startswith("global_load_dwordx2") for ln in prologue) == 1     # the table, once
-    assert sum(ln.startswith("v_readlane_b32") for ln in prologue) >= 2 * w
-    loads = [ln for ln in body if re.match(r"(buffer|global|flat)_load", ln)]
+    loads = [ln for ln in body if ln.startswith("buffer_load")]
     stores = [i for i, ln in enumerate(body) if ln.startswith("buffer_store")]
-    assert len(loads) == 2 * w * vpt and len(stores) == 2 * w * vpt   # two tiles per unrolled trip
+    assert len(loads) == 2 * vpt and len(stores) == 2 * vpt   # one chunk tile per step, two steps per trip
+    reads = [ln for ln in body if ln.startswith("v_readlane_b32")]
+    assert len(reads) == 4 and all(re.fullmatch(r"v_readlane_b32 s\d+, v\d+, s\d+", ln) for ln in reads), reads
     prev = 0
     for i in stores:
         assert not [ln for ln in body[prev:i] if ln.startswith("s_waitcnt") and "vmcnt(0)" in ln]

@@ -171,6 +171,21 @@ def test_all_to_all_tiny_sweep(W, start, stride, M, N):
     _a2a(8, _size(W, M, N, e, off), W, start, stride, M, N, dtype, off, chosen, programs, seed=W + M + N)
 
 
+@pytest.mark.parametrize("W,start,stride", [(3, 1, 2), (8, 0, 1)])
+@pytest.mark.parametrize("M,N,dtype,tile,vpt", [(100, 1000, "f16", (32, 256), 4), (77, 4100, "bf16", (16, 512), 8),
+                                                (50, 520, "f32", (8, 512), 4), (40, 3000, "f32", (16, 512), 8)])
+def test_all_to_all_four_and_eight_vectors_per_thread(W, start, stride, M, N, dtype, tile, vpt):
+    """Larger tiles: 4 or 8 vector accesses per thread and chunk tile (ragged rows and columns)."""
+    e = E[dtype]
+    off = 64
+    for programs in (5, 256):
+        p = ag.plan_all_to_all(ag.Geometry(slab_addr=1 << 32, bytes_per_rank=_size(W, M, N, e, off), n_ranks=8,
+                                           rank=start, num_cus=256), W, start, stride, 1 << 44, off, M, N, dtype,
+                               tile[0], tile[1], programs)
+        assert p.vectors_per_thread == vpt
+        _a2a(8, _size(W, M, N, e, off), W, start, stride, M, N, dtype, off, tile, programs, seed=W + M + programs)
+
+
 def test_all_to_all_row_view():
     # chunks of 1000 x 4100 fp16: rows of 8200 bytes, chunks of 512,500 16-byte vectors, so the kernel walks
     # them as rows of 4000 elements with 16-byte vectors
