@@ -673,8 +673,8 @@ CopyFn pick_world(int w, int vpt, int g, bool part, bool wide)
     }
 }
 
-// ---- all-to-all instantiations: VEC x W x VPT with VEC*VPT <= 32 bytes per
-// thread and chunk tile (two register sets of W such tiles stay live)
+// ---- all-to-all instantiations: VEC x W x VPT, 1 to 8 vectors per thread
+// and chunk tile (two register sets of one tile each stay live)
 template <int VEC, int W>
 CopyFn pick_a2a_vpt(int vpt, bool wide)
 {
