@@ -261,7 +261,8 @@ def _context(args, stream, timed, head):
     * its variants: destination groups 1/2/4 and the partitioned schedule at 64/128/256 programs;
     * the 1024x4096 all-gather at 64/128/256 programs (75 MB per call: partly held by the last-level
       cache, so its rate exceeds what HBM sustains for the larger shape);
-    * the all-to-all: W=8, 8 chunks of 1024x4096 fp16 per rank, tile and partitioned schedules;
+    * the all-to-all: W=8, 8 chunks of 1024x4096 fp16 per rank, tile and partitioned schedules, and 8 chunks
+      of 2048x8192 in both tile orders at 256 / 128 / 64 programs;
     * the edge shapes: 1000x4100 fp16 (partial last column tile) at W=8, and the strided group of ranks
       1, 3, 5, 7 (W=4) at 1000x4100 and 16384x8192.
     """
@@ -329,7 +330,8 @@ def _context(args, stream, timed, head):
 
 
 def _all_to_all(sub, stream, timed):
-    """The all-to-all on its own heap: W=8, 8 chunks of 1024x4096 fp16 per rank, tile and partitioned schedules."""
+    """The all-to-all on its own heap: W=8, 8 chunks of 1024x4096 fp16 per rank, tile and partitioned schedules;
+    then 8 chunks of 2048x8192 per rank in both tile orders."""
     from gemm_all_gather_amd import binding as ag
 
     # all-to-all: each rank sends 8 chunks of 1024x4096 fp16 (64 MiB per rank); 8x512 tiles, two 16-byte
@@ -360,6 +362,25 @@ def _all_to_all(sub, stream, timed):
                                             schedule="partitioned", stream=stream) for j in range(AG_W)], sub)
     res["partitioned_16x512_256_programs_GBs"] = round(AG_W * a2a_bytes / (ms / 1e3) / 1e9, 1)
     a2a.close()
+
+    # a long exchange: 8 chunks of 2048x8192 fp16 per rank (256 MiB), 8x512 tiles, in the library's tile
+    # order and in the other one, at 256 / 128 / 64 programs
+    bm, bn = 2048, 8192
+    big = _Workload(AG_W * bm, bn, "f16", seed=6, out_bytes=AG_W * bm * bn * 2)
+    big_bytes = 2 * AG_W * bm * bn * 2
+    out = {}
+    for P in (256, 128, 64):
+        auto = ag.plan_all_to_all(big.geom, AG_W, 0, 1, big.ins[0], 0, bm, bn, "f16", *A2A_TILE, P)
+        row = {}
+        for order in ("stride", "tickets"):
+            ms, _ = timed(lambda: [ag.all_to_all_ex(big.views[j], AG_W, 0, 1, big.ins[j], 0, bm, bn, "f16", *A2A_TILE, P,
+                                                    stream=stream, tile_order=order) for j in range(AG_W)], sub)
+            row[order] = {"GBs": round(AG_W * big_bytes / (ms / 1e3) / 1e9, 1),
+                          "us_per_call": round(ms * 1e3 / AG_W, 2)}
+        row["library_order"] = "tickets" if auto.tile_order == ag.AG_ORDER_TICKETS else "stride"
+        out[str(P)] = row
+    res[f"{bm}x{bn}_8x512_by_programs"] = out
+    big.close()
     return res
 
 

@@ -327,8 +327,13 @@ __global__ __launch_bounds__(1024) void ag_copy_kernel(CopyKernelArgs a)
 // stores in flight keep the HBM write streams denser (W=8, 16384x8192 fp16,
 // 256 programs: 360 against 387 us per call in a measured replica); with half
 // the CUs the wait costs more than it saves.
-template <int VEC, int W, int VPT, int G, bool WIDE, bool DRAIN>
-__global__ __launch_bounds__(256) void ag_copy_ticket_kernel(CopyKernelArgs a)
+//
+// A2A (the all-to-all in ticket order): the tiles are the W chunk copies as
+// one sequence, destination by destination, as in ag_a2a_kernel; each tile
+// has one source (chunk (g + i) mod W) and one destination (i) instead of
+// one source and W destinations.
+template <int VEC, int W, int VPT, int G, bool WIDE, bool DRAIN, bool A2A>
+__device__ __forceinline__ void ticket_copy(const CopyKernelArgs& a)
 {
     constexpr int kAux = WIDE ? AG_COPY_STORE_AUX_WIDE : AG_COPY_STORE_AUX;
     using VT = Vec<VEC>;
@@ -336,11 +341,14 @@ __global__ __launch_bounds__(256) void ag_copy_ticket_kernel(CopyKernelArgs a)
     __shared__ uint32_t s_ticket[2];
 
     const uint32_t row_bytes = static_cast<uint32_t>(a.row_bytes);
-    const uint32_t block_bytes = a.rows * row_bytes;             // < 2^31 (planner)
+    const uint32_t block_bytes = a.rows * row_bytes;             // < 2^31 (planner); one chunk for A2A
     const uint32_t tile_rows_bytes = a.tile_m * row_bytes;       // bytes from one tile row to the next
     const uint32_t last_col_bytes = row_bytes - (a.tiles_n - 1u) * a.tile_row_bytes;
     const uint64_t input = reinterpret_cast<uint64_t>(a.input);
     uint32_t* const counter = a.tickets;
+    const uint32_t per_dest = a.total_tiles;                     // A2A: tiles of one chunk
+    const uint32_t total = A2A ? per_dest * static_cast<uint32_t>(W) : per_dest;   // < 2^31 (planner)
+    const uint32_t chunk_rows_bytes = (per_dest / a.tiles_n) * tile_rows_bytes;    // A2A: a chunk's tile rows
 
     const uint32_t lane = threadIdx.x;
     const uint32_t vpr_mask = (1u << a.vecs_per_row_log2) - 1u;
@@ -351,29 +359,47 @@ __global__ __launch_bounds__(256) void ag_copy_ticket_kernel(CopyKernelArgs a)
         lane_col[j] = (idx & vpr_mask) * VEC;
         lane_off[j] = (idx >> a.vecs_per_row_log2) * row_bytes + lane_col[j];
     }
-    // Walk the G tiles first, first+1, ... (row-major over the tile grid), calling f(b, off, records, lim)
-    // for each: its byte offset in the block, the bytes addressable from there (0 past the last tile:
-    // every access dropped) and the bytes of its row a lane may touch (the last tile column's width).
+    // Walk the G tiles first, first+1, ... (row-major over the tile grid; A2A: chunk after chunk), calling
+    // f(b, i, off, records, lim) for each: the destination index (A2A; 0 otherwise and past the last
+    // tile), its byte offset in the block, the bytes addressable from there (0 past the last tile: every
+    // access dropped) and the bytes of its row a lane may touch (the last tile column's width).
     auto for_tiles = [&](uint32_t first, auto&& f) {
-        uint32_t tm = first / a.tiles_n;
-        uint32_t tn = first - tm * a.tiles_n;
+        uint32_t i = 0, t = first;
+        if constexpr (A2A) {
+            i = first / per_dest;
+            t = first - i * per_dest;
+        }
+        uint32_t tm = t / a.tiles_n;
+        uint32_t tn = t - tm * a.tiles_n;
         uint32_t row0 = tm * tile_rows_bytes;
 #pragma unroll
         for (int b = 0; b < G; ++b) {
-            const bool valid = first + static_cast<uint32_t>(b) < a.total_tiles;
+            const bool valid = first + static_cast<uint32_t>(b) < total;
             const uint32_t off = valid ? row0 + tn * a.tile_row_bytes : 0u;
             const uint32_t lim = tn + 1u == a.tiles_n ? last_col_bytes : 0xffffffffu;
-            f(b, off, valid ? block_bytes - off : 0u, lim);
+            f(b, valid ? i : 0u, off, valid ? block_bytes - off : 0u, lim);
             if (++tn == a.tiles_n) {
                 tn = 0;
                 row0 += tile_rows_bytes;
+                if constexpr (A2A) {
+                    if (row0 == chunk_rows_bytes) {   // on to the next destination's chunk
+                        row0 = 0;
+                        ++i;
+                    }
+                }
             }
         }
     };
     auto lane_offset = [&](int j, uint32_t lim) { return lane_col[j] < lim ? lane_off[j] : kOutOfRange; };
     auto load_batch = [&](uint32_t first, V (&v)[G][VPT]) {
-        for_tiles(first, [&](int b, uint32_t off, uint32_t records, uint32_t lim) {
-            const __amdgpu_buffer_rsrc_t src = make_rsrc(input + off, records);
+        for_tiles(first, [&](int b, uint32_t i, uint32_t off, uint32_t records, uint32_t lim) {
+            uint64_t base = input;
+            if constexpr (A2A) {   // chunk (g + i) mod W is meant for destination i
+                uint32_t gi = static_cast<uint32_t>(a.group_rank) + i;
+                if (gi >= static_cast<uint32_t>(W)) gi -= W;
+                base += static_cast<uint64_t>(gi) * block_bytes;
+            }
+            const __amdgpu_buffer_rsrc_t src = make_rsrc(base + off, records);
 #pragma unroll
             for (int j = 0; j < VPT; ++j) v[b][j] = VT::load(src, lane_offset(j, lim));
         });
@@ -411,7 +437,7 @@ __global__ __launch_bounds__(256) void ag_copy_ticket_kernel(CopyKernelArgs a)
     int slot = 1;
     V va[G][VPT], vb[G][VPT];
     uint32_t ta = first, tb = 0;
-    if (ta < a.total_tiles) {
+    if (ta < total) {
         load_batch(ta, va);
         if constexpr (!DRAIN) {
             tb = post(threadIdx.x == 0 ? take() : 0u, slot);
@@ -419,8 +445,8 @@ __global__ __launch_bounds__(256) void ag_copy_ticket_kernel(CopyKernelArgs a)
             load_batch(tb, vb);
         }
 
-        uint64_t dest[W];
-        {
+        uint64_t dest[A2A ? 1 : W];
+        if constexpr (!A2A) {
             const uint32_t lo = static_cast<uint32_t>(table_entry), hi = static_cast<uint32_t>(table_entry >> 32);
             const uint64_t local_base = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(hi, W))) << 32) |
                                         static_cast<uint32_t>(__builtin_amdgcn_readlane(lo, W));
@@ -432,13 +458,27 @@ __global__ __launch_bounds__(256) void ag_copy_ticket_kernel(CopyKernelArgs a)
                 dest[i] = out_local + static_cast<uint64_t>(static_cast<int64_t>(b - local_base));
             }
         }
+        // A2A: lane i < W holds this rank's block in destination i's region (its heap base plus the
+        // block offset), set once; a tile reads its destination's with readlane
+        const uint64_t dest_lane = table_entry + a.rank_block_offset;
         auto store_batch = [&](uint32_t first_tile, const V (&v)[G][VPT]) {
-            for_tiles(first_tile, [&](int b, uint32_t off, uint32_t records, uint32_t lim) {
-#pragma unroll
-                for (int i = 0; i < W; ++i) {   // local region first, then the rotated peers
-                    const __amdgpu_buffer_rsrc_t dst = make_rsrc(dest[i] + off, records);
+            for_tiles(first_tile, [&](int b, uint32_t di, uint32_t off, uint32_t records, uint32_t lim) {
+                if constexpr (A2A) {
+                    const int li = static_cast<int>(di);
+                    const int lo = static_cast<int>(static_cast<uint32_t>(dest_lane));
+                    const int hi = static_cast<int>(static_cast<uint32_t>(dest_lane >> 32));
+                    const uint64_t d = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(hi, li))) << 32) |
+                                       static_cast<uint32_t>(__builtin_amdgcn_readlane(lo, li));
+                    const __amdgpu_buffer_rsrc_t dst = make_rsrc(d + off, records);
 #pragma unroll
                     for (int j = 0; j < VPT; ++j) VT::template store<kAux>(v[b][j], dst, lane_offset(j, lim));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < W; ++i) {   // local region first, then the rotated peers
+                        const __amdgpu_buffer_rsrc_t dst = make_rsrc(dest[i] + off, records);
+#pragma unroll
+                        for (int j = 0; j < VPT; ++j) VT::template store<kAux>(v[b][j], dst, lane_offset(j, lim));
+                    }
                 }
             });
         };
@@ -450,12 +490,12 @@ __global__ __launch_bounds__(256) void ag_copy_ticket_kernel(CopyKernelArgs a)
                 slot ^= 1;
                 load_batch(tb, vb);
                 store_batch(ta, va);
-                if (tb >= a.total_tiles) break;
+                if (tb >= total) break;
                 ta = post(threadIdx.x == 0 ? take() : 0u, slot);
                 slot ^= 1;
                 load_batch(ta, va);
                 store_batch(tb, vb);
-                if (ta >= a.total_tiles) break;
+                if (ta >= total) break;
             }
         } else {
             // Invariant: va holds batch ta (in hand, ta < total), vb batch tb (loading); tickets rise.
@@ -463,7 +503,7 @@ __global__ __launch_bounds__(256) void ag_copy_ticket_kernel(CopyKernelArgs a)
             // other lanes, so nothing overwrites its register while the atomic is in flight and its wait
             // (at the LDS write, after the stores) covers only what was issued before it.
             for (;;) {
-                bool more = tb < a.total_tiles;
+                bool more = tb < total;
                 uint32_t tk;
                 if (more && threadIdx.x == 0) tk = take();   // the batch after tb, before ta's stores
                 store_batch(ta, va);
@@ -472,7 +512,7 @@ __global__ __launch_bounds__(256) void ag_copy_ticket_kernel(CopyKernelArgs a)
                 slot ^= 1;
                 load_batch(ta, va);
 
-                more = ta < a.total_tiles;
+                more = ta < total;
                 if (more && threadIdx.x == 0) tk = take();
                 store_batch(tb, vb);
                 if (!more) break;
@@ -490,6 +530,19 @@ __global__ __launch_bounds__(256) void ag_copy_ticket_kernel(CopyKernelArgs a)
             __hip_atomic_store(counter + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+}
+
+template <int VEC, int W, int VPT, int G, bool WIDE, bool DRAIN>
+__global__ __launch_bounds__(256) void ag_copy_ticket_kernel(CopyKernelArgs a)
+{
+    ticket_copy<VEC, W, VPT, G, WIDE, DRAIN, false>(a);
+}
+
+// The all-to-all in ticket order (16-byte vectors).
+template <int W, int VPT, int G, bool WIDE, bool DRAIN>
+__global__ __launch_bounds__(256) void ag_a2a_ticket_kernel(CopyKernelArgs a)
+{
+    ticket_copy<16, W, VPT, G, WIDE, DRAIN, true>(a);
 }
 
 // All-to-all: destination i (group member (g + i) mod W, i = 0 the local
@@ -759,6 +812,40 @@ CopyFn pick_ticket(int vec, int w, int vpt, int ticket, bool wide, bool drain)
     }
 }
 
+// ---- ticket-order all-to-all instantiations: 16-byte vectors, W = 1..8; a tile moves its bytes twice
+// (one read, one write), so the planner's 96 KiB per ticket is 16 tiles of one vector per thread and 8
+// of two, whatever the launch
+template <int W, int VPT, int G>
+CopyFn pick_a2a_ticket_policy(bool wide, bool drain)
+{
+    if (drain) return wide ? ag_a2a_ticket_kernel<W, VPT, G, true, true> : ag_a2a_ticket_kernel<W, VPT, G, false, true>;
+    return wide ? ag_a2a_ticket_kernel<W, VPT, G, true, false> : ag_a2a_ticket_kernel<W, VPT, G, false, false>;
+}
+
+template <int W>
+CopyFn pick_a2a_ticket_vpt(int vpt, int ticket, bool wide, bool drain)
+{
+    if (vpt == 1 && ticket == 16) return pick_a2a_ticket_policy<W, 1, 16>(wide, drain);
+    if (vpt == 2 && ticket == 8) return pick_a2a_ticket_policy<W, 2, 8>(wide, drain);
+    return nullptr;
+}
+
+CopyFn pick_a2a_ticket(int vec, int w, int vpt, int ticket, bool wide, bool drain)
+{
+    if (vec != 16) return nullptr;
+    switch (w) {
+    case 1: return pick_a2a_ticket_vpt<1>(vpt, ticket, wide, drain);
+    case 2: return pick_a2a_ticket_vpt<2>(vpt, ticket, wide, drain);
+    case 3: return pick_a2a_ticket_vpt<3>(vpt, ticket, wide, drain);
+    case 4: return pick_a2a_ticket_vpt<4>(vpt, ticket, wide, drain);
+    case 5: return pick_a2a_ticket_vpt<5>(vpt, ticket, wide, drain);
+    case 6: return pick_a2a_ticket_vpt<6>(vpt, ticket, wide, drain);
+    case 7: return pick_a2a_ticket_vpt<7>(vpt, ticket, wide, drain);
+    case 8: return pick_a2a_ticket_vpt<8>(vpt, ticket, wide, drain);
+    default: return nullptr;
+    }
+}
+
 CopyFn pick_kernel(int kind, int vec, int w, int g, int vpt, bool part, bool wide)
 {
     // the partitioned all-to-all runs the partitioned copy kernel (one destination per program)
@@ -788,8 +875,9 @@ bool copy_supported(int kind, int vec_bytes, int dests, int group, int vpt, bool
     return pick_kernel(kind, vec_bytes, dests, group, vpt, partitioned, false) != nullptr;
 }
 
-bool copy_ticket_supported(int vec_bytes, int dests, int vpt, int ticket)
+bool copy_ticket_supported(int kind, int vec_bytes, int dests, int vpt, int ticket)
 {
+    if (kind == kCopyAllToAll) return pick_a2a_ticket(vec_bytes, dests, vpt, ticket, false, false) != nullptr;
     return pick_ticket(vec_bytes, dests, vpt, ticket, false, false) != nullptr;
 }
 
@@ -842,9 +930,12 @@ hipError_t noalloc_tickets(int rank, hipStream_t stream, uint32_t** out)
 hipError_t launch_copy(const CopyLaunch& l, hipStream_t stream)
 {
     if (l.ticket != 0) {
-        CopyFn fn = l.kind == kCopyAllGather && l.group == 0 && !l.args.partitioned && l.args.slices == 1
-                        ? pick_ticket(l.vec_bytes, l.dests, l.vpt, l.ticket, l.wide != 0, l.drain != 0)
-                        : nullptr;
+        CopyFn fn = nullptr;
+        if (l.group == 0 && !l.args.partitioned && l.args.slices == 1) {
+            if (l.kind == kCopyAllGather) fn = pick_ticket(l.vec_bytes, l.dests, l.vpt, l.ticket, l.wide != 0, l.drain != 0);
+            if (l.kind == kCopyAllToAll)
+                fn = pick_a2a_ticket(l.vec_bytes, l.dests, l.vpt, l.ticket, l.wide != 0, l.drain != 0);
+        }
         if (fn == nullptr || l.grid < 1 || l.args.tickets == nullptr) return hipErrorInvalidValue;
         hipLaunchKernelGGL(fn, dim3(l.grid), dim3(256), 0, stream, l.args);
         return hipGetLastError();

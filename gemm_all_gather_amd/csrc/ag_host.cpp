@@ -464,8 +464,8 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
         return fail(AG_ERR_INVALID_ARG, "unknown schedule %d", opt.schedule);
     if (opt.tile_order != AG_ORDER_AUTO && opt.tile_order != AG_ORDER_STRIDE && opt.tile_order != AG_ORDER_TICKETS)
         return fail(AG_ERR_INVALID_ARG, "unknown tile_order %d", opt.tile_order);
-    if (opt.tile_order != AG_ORDER_AUTO && (a2a || opt.schedule != AG_SCHEDULE_TILES))
-        return fail(AG_ERR_INVALID_ARG, "tile_order applies to the all-gather's tile schedule only");
+    if (opt.tile_order != AG_ORDER_AUTO && opt.schedule != AG_SCHEDULE_TILES)
+        return fail(AG_ERR_INVALID_ARG, "tile_order applies to the tile schedule only");
     if (opt.dest_group < 0) return fail(AG_ERR_INVALID_ARG, "dest_group %d < 0", opt.dest_group);
     if (opt.dest_group != 0 && opt.dest_group != 1 && opt.dest_group != 2 && opt.dest_group != 4)
         return fail(AG_ERR_UNSUPPORTED, "dest_group %d: 0, 1, 2 or 4 are supported", opt.dest_group);
@@ -579,6 +579,8 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
     // 16 tiles per program: 15.9 against 11.8 us per call).
     int ticket = 0;
     const int tvpt = static_cast<int>(tile_vecs / 256);   // 16-byte vectors per thread and tile (tickets)
+    // the tiles the programs share out: the all-to-all's W chunk copies are one sequence of W x total
+    const uint64_t seq_tiles = a2a ? total * static_cast<uint64_t>(W) : total;
     {
         // tiles per ticket: the ticket kernels exist for 3, 4, 8 and 16 tiles with one vector per
         // thread and 2, 4 and 8 with two
@@ -586,7 +588,8 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
         static constexpr int kSizesVpt2[] = {2, 4, 8};
         const int* sizes = tvpt == 2 ? kSizesVpt2 : kSizesVpt1;
         const int n_sizes = tvpt == 2 ? 3 : 4;
-        const uint64_t hbm_bytes_per_tile = tile_vecs * vec * (1 + static_cast<uint64_t>(W));
+        // HBM bytes a tile moves: read once, then written W times (the all-to-all: once)
+        const uint64_t hbm_bytes_per_tile = tile_vecs * vec * (a2a ? 2 : 1 + static_cast<uint64_t>(W));
         int g_floor = sizes[n_sizes - 1];
         for (int i = 0; i < n_sizes; ++i) {
             if (sizes[i] * hbm_bytes_per_tile >= AG_TICKETS_MIN_BYTES) {
@@ -603,20 +606,29 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
         g = std::max(g, g_floor);
         // the ticket kernel's tile offsets are 32-bit: every tile row of the block must lie below 2 GiB
         const bool small = tiles_m * tile_m * view_row_bytes < (uint64_t{1} << 31);
-        const bool fits = !part && !a2a && p.dest_group == 0 && small && ag::copy_ticket_supported(vec, W, tvpt, g);
+        const bool fits = !part && p.dest_group == 0 && small && ag::copy_ticket_supported(kind, vec, W, tvpt, g);
         if (opt.tile_order == AG_ORDER_TICKETS) {
             if (!fits)
                 return fail(AG_ERR_UNSUPPORTED, "no ticket-order kernel for this call (%d-byte vectors, %d per thread, "
                             "destination group %d, %s 2 GiB of tile rows)", vec, tvpt, p.dest_group,
                             small ? "under" : "not under");
             ticket = g;
-        } else if (opt.tile_order == AG_ORDER_AUTO && fits && total >= AG_TICKETS_MIN_TILES_PER_PROGRAM * programs) {
-            ticket = g;
+        } else if (opt.tile_order == AG_ORDER_AUTO && fits) {
+            // The all-gather takes tickets from 64 tiles per program.  The all-to-all's grid stride already
+            // keeps only two or four streams open (one chunk at a time), so tickets pay off only where few
+            // vectors are in flight per CU and the call is long: programs x vectors per thread below twice
+            // the CU count, and 64 tiles per program per vector.  Measured at W=8, fp16, us per call, grid
+            // stride / tickets: 8 chunks of 2048x8192 with 8x512 tiles 85.1 / 87.4 at 256 programs, 105.7 /
+            // 98.3 at 128, 186.9 / 146.9 at 64; with 8x256 tiles 104.5 / 89.1 at 256; 8 chunks of 1024x4096
+            // with 8x512 tiles 22.9 / 27.1 at 256, 28.1 / 30.3 at 128, 48.8 / 42.2 at 64.
+            const uint64_t per_vec = a2a ? static_cast<uint64_t>(tvpt) : 1;
+            const bool few_in_flight = !a2a || programs * per_vec < 2 * static_cast<uint64_t>(geom->num_cus);
+            if (few_in_flight && seq_tiles >= AG_TICKETS_MIN_TILES_PER_PROGRAM * per_vec * programs) ticket = g;
         }
     }
     uint64_t slices = 1, grid = 0;
     if (ticket) {
-        grid = std::min<uint64_t>(programs, ceil_div(total, static_cast<uint64_t>(ticket)));
+        grid = std::min<uint64_t>(programs, ceil_div(seq_tiles, static_cast<uint64_t>(ticket)));
     } else if (part) {
         // W equal sets of programs, one per destination, each walking all tiles
         const uint64_t per_dest = std::min<uint64_t>(std::max<uint64_t>(programs / W, 1), total);
@@ -626,8 +638,7 @@ ag_status_t plan_copy(const ag_heap_geometry_t* geom, int kind, int W, int rank_
         const uint64_t max_slices = 2 * programs < static_cast<uint64_t>(geom->num_cus) ? kCopyNarrowSlices
                                                                                      : static_cast<uint64_t>(kCopyMaxSlices);
         while (!a2a && slices < max_slices && programs * slices * 2 <= total) slices *= 2;
-        // (the all-to-all walks W x total tiles: the block's tiles of each of the W chunks)
-        grid = std::min<uint64_t>(programs, a2a ? total * static_cast<uint64_t>(W) : ceil_div(total, slices));
+        grid = std::min<uint64_t>(programs, ceil_div(seq_tiles, slices));
     }
     if (grid >= (uint64_t{1} << 31)) return fail(AG_ERR_UNSUPPORTED, "n_programs too large");
     const int vpt = static_cast<int>(tile_vecs / 256);

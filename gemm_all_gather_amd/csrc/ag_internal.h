@@ -49,8 +49,9 @@ struct CopyLaunch {
 
 // Whether the launcher has a kernel for (kind, vec, dests, group, vpt, schedule) (host-only).
 bool copy_supported(int kind, int vec_bytes, int dests, int group, int vpt, bool partitioned);
-// Whether the ticket-order all-gather kernel exists for (vec, dests, vpt, tiles per ticket) (host-only).
-bool copy_ticket_supported(int vec_bytes, int dests, int vpt, int ticket);
+// Whether the ticket-order kernel of kind (all-gather or all-to-all) exists for (vec, dests, vpt, tiles per
+// ticket) (host-only).
+bool copy_ticket_supported(int kind, int vec_bytes, int dests, int vpt, int ticket);
 hipError_t launch_copy(const CopyLaunch& l, hipStream_t stream);
 
 // Tile counters of ag_all_gather_noalloc: rank indices below kNoAllocMaxRanks have a counter pair in a

@@ -109,19 +109,24 @@ typedef enum ag_schedule {
     AG_SCHEDULE_PARTITIONED = 1  /* each program owns one destination and walks the tiles for it alone */
 } ag_schedule_t;
 
-/* Order in which the persistent programs of AG_SCHEDULE_TILES take their tiles.  The result does
- * not depend on it. */
+/* Order in which the persistent programs of AG_SCHEDULE_TILES take their tiles (the all-to-all's
+ * tiles: the W chunk copies as one sequence, destination by destination).  The result does not
+ * depend on it. */
 typedef enum ag_tile_order {
-    AG_ORDER_AUTO = 0,     /* the library's choice: AG_ORDER_TICKETS for calls of at least 64 tiles per
-                              program where a ticket kernel exists, AG_ORDER_STRIDE otherwise */
+    AG_ORDER_AUTO = 0,     /* the library's choice: AG_ORDER_TICKETS where a ticket kernel exists and,
+                              for the all-gather, the call has at least 64 tiles per program; for the
+                              all-to-all, at least 64 tiles per program and vector per thread with
+                              programs x vectors per thread below twice the CU count.
+                              AG_ORDER_STRIDE otherwise */
     AG_ORDER_STRIDE = 1,   /* fixed grid stride: program p takes tiles p, p + P, p + 2P, ... */
     AG_ORDER_TICKETS = 2   /* programs take G consecutive tiles at a time from a device counter of the
                               calling rank, in increasing tile order; 16-byte vectors, one or two per
                               thread and tile, no destination groups, every tile row of the block below
                               2 GiB.  G is one of 3, 4, 8, 16 (one vector per thread) or 2, 4, 8 (two):
-                              the smallest whose tiles, read once and written W times, move at least
-                              96 KiB of HBM traffic (the largest where none does), and on launches with
-                              fewer programs than CUs at least the largest of 16, 8 and 4 (within those
+                              the smallest whose tiles move at least 96 KiB of HBM traffic (the
+                              all-gather's read once and written W times, the all-to-all's read and
+                              written once; the largest where none does), and on launches with fewer
+                              programs than CUs at least the largest of 16, 8 and 4 (within those
                               sizes) with G x programs <= 1024.  When programs x vectors per thread
                               reach three quarters of the CU count, each program takes its next ticket
                               after the stores of the batch in hand (plan.ticket_wait) */
@@ -133,7 +138,7 @@ typedef struct ag_copy_options {
                              1, 2 or 4 (< W): store that many destinations, then wait until the
                              stores before them have completed, then the next group */
     int32_t schedule;     /* ag_schedule_t */
-    int32_t tile_order;   /* ag_tile_order_t (all-gather with AG_SCHEDULE_TILES only; else 0) */
+    int32_t tile_order;   /* ag_tile_order_t (AG_SCHEDULE_TILES only; else 0) */
     int32_t reserved[5];  /* must be 0 */
 } ag_copy_options_t;
 
@@ -287,10 +292,10 @@ ag_status_t ag_plan_all_gather(const ag_heap_geometry_t* geom, int W, int rank_s
  *               destination groups: AG_ORDER_STRIDE or AG_ORDER_TICKETS force
  *               the order (AG_ERR_UNSUPPORTED where no ticket kernel fits the
  *               call: vectors other than 16 bytes or more than two per thread,
- *               destination groups, the partitioned schedule).  Ticket order
- *               at 256 programs, W=8, 16384x8192 fp16: 6.4 TB/s against 5.3
- *               for the grid stride; below about 64 tiles per program the
- *               counter's round trips cost more than they save.
+ *               destination groups).  Ticket order at 256 programs, W=8,
+ *               16384x8192 fp16: 6.77 TB/s against 5.28 for the grid stride;
+ *               below about 64 tiles per program the counter's round trips
+ *               cost more than they save.
  * Plan: ag_plan_all_gather_ex reports dest_group, schedule and tile_order as
  * applied, and bytes_read of the schedule (W times the input when
  * partitioned).
@@ -357,8 +362,8 @@ ag_status_t ag_plan_all_to_all(const ag_heap_geometry_t* geom, int W, int rank_s
                                ag_dtype_t dtype, int tile_m, int tile_n, int n_programs, ag_plan_t* plan);
 
 /* ag_all_to_all with options (NULL or all-zero = ag_all_to_all).  Same
- * result.  dest_group and tile_order must be 0 (AG_ERR_INVALID_ARG
- * otherwise).  schedule
+ * result.  dest_group must be 0 (AG_ERR_INVALID_ARG otherwise).  tile_order
+ * as for ag_all_gather_ex (AG_SCHEDULE_TILES only).  schedule
  * AG_SCHEDULE_PARTITIONED (the partitioned schedule of ag_all_gather_ex
  * applied to the exchange): program p owns destination i = p mod W of the
  * rotated order and copies chunk (g + i) mod W there, the programs of one

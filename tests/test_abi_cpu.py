@@ -563,9 +563,28 @@ def test_plan_tickets_need_16_byte_vectors():
     assert p.vec_bytes == 8 and p.tile_order == ag.AG_ORDER_STRIDE
 
 
-def test_plan_all_to_all_takes_no_tile_order():
-    got, _ = status_of(ag.plan_all_to_all_ex, geom(), 8, 0, 1, INPUT, 0, 128, 4096, "f16", 0, 0, 0,
-                       tile_order="tickets")
-    assert got == ag.AG_ERR_INVALID_ARG
-    p = ag.plan_all_to_all(geom(), 8, 0, 1, INPUT, 0, 1024, 4096, "f16", 0, 0, 256)
-    assert p.tile_order == ag.AG_ORDER_STRIDE and p.tiles_per_ticket == 0
+def test_plan_all_to_all_tile_order():
+    """The all-to-all's W chunk copies are one sequence of W x (tiles per chunk) tiles shared by the
+    programs; in ticket order each tile moves its bytes twice (read, write), so 96 KiB of traffic per
+    ticket is 16 tiles of 8x256 fp16 and 8 of 8x512."""
+    p = ag.plan_all_to_all_ex(geom(), 8, 0, 1, INPUT, 0, 128, 4096, "f16", 0, 0, 0, tile_order="tickets")
+    assert p.tile_order == ag.AG_ORDER_TICKETS and p.tiles_per_ticket == 16
+    assert p.total_tiles == 16 * 16 and p.n_programs == 8 * 16 * 16 // 16
+    p = ag.plan_all_to_all_ex(geom(), 8, 0, 1, INPUT, 0, 128, 4096, "f16", 8, 512, 0, tile_order="tickets")
+    assert p.vectors_per_thread == 2 and p.tiles_per_ticket == 8 and p.n_programs == 8 * 16 * 8 // 8
+    p = ag.plan_all_to_all_ex(geom(), 8, 0, 1, INPUT, 0, 128, 4096, "f16", 0, 0, 0, tile_order="stride")
+    assert p.tile_order == ag.AG_ORDER_STRIDE and p.n_programs == 256
+    # the library's choice: tickets where programs x vectors per thread stay below twice the CU count and
+    # there are 64 tiles of the sequence per program and vector
+    big = geom(bytes_per_rank=8 * 2048 * 8192 * 2 + MiB)
+    for M, N, g, tile, progs, want in ((1024, 4096, geom(), (8, 512), 256, 0), (1024, 4096, geom(), (8, 512), 128, 0),
+                                       (1024, 4096, geom(), (8, 512), 64, 8), (1024, 4096, geom(), (8, 256), 192, 16),
+                                       (2048, 8192, big, (8, 512), 256, 0), (2048, 8192, big, (8, 512), 192, 8),
+                                       (2048, 8192, big, (8, 512), 128, 8), (2048, 8192, big, (8, 256), 256, 16)):
+        p = ag.plan_all_to_all(g, 8, 0, 1, INPUT, 0, M, N, "f16", *tile, progs)
+        assert p.tiles_per_ticket == want, (M, tile, progs, p.tiles_per_ticket)
+        assert p.tile_order == (ag.AG_ORDER_TICKETS if want else ag.AG_ORDER_STRIDE)
+    for kw in (dict(schedule="partitioned"), dict(dest_group=2)):
+        got, _ = status_of(ag.plan_all_to_all_ex, geom(), 8, 0, 1, INPUT, 0, 128, 4096, "f16", 0, 0, 0,
+                           tile_order="tickets", **kw)
+        assert got == ag.AG_ERR_INVALID_ARG

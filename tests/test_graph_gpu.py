@@ -81,21 +81,24 @@ def test_all_gather_in_ticket_order_replayed(noalloc):
         th.close()
 
 
-def test_all_to_all_replayed():
+@pytest.mark.parametrize("order", ["stride", "tickets"])
+def test_all_to_all_replayed(order):
     require_gpu()
     W, Mc, N = 4, 64, 1024
     S = ((W * Mc * N * 2 + 4096) // 256 + 1) * 256
     th = TorchHeap(4, S)
     try:
         dev = [to_device(gen.random_bit_patterns((W * Mc, N), 2, 90, j)) for j in range(W)]
+        p = ag.plan_all_to_all_ex(th.view(0).geometry(), W, 0, 1, dev[0], 0, Mc, N, "f16", 0, 0, 0, tile_order=order)
+        assert p.tile_order == (ag.AG_ORDER_TICKETS if order == "tickets" else ag.AG_ORDER_STRIDE)
 
         def calls(stream):
             for j in range(W):
-                ag.all_to_all(th.view(j), W, 0, 1, dev[j], 0, Mc, N, "f16", 0, 0, 0, stream=stream)
+                ag.all_to_all_ex(th.view(j), W, 0, 1, dev[j], 0, Mc, N, "f16", 0, 0, 0, stream=stream, tile_order=order)
 
         g = _capture(calls)
         _replays(th, dev, lambda rep: [gen.random_bit_patterns((W * Mc, N), 2, 91 + rep, j) for j in range(W)], g,
-                 lambda before, ins: all_to_all_oracle(before, S, ins, 0, 1, 0), "all_to_all graph")
+                 lambda before, ins: all_to_all_oracle(before, S, ins, 0, 1, 0), f"all_to_all graph ({order})")
     finally:
         th.close()
 

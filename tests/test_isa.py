@@ -229,6 +229,37 @@ def test_ticket_kernel_hoists_bases_and_never_drains_before_a_store(asm, w, vpt,
     assert _meta(asm["ag_copy.hip"], sym)["scratch"] == 0
 
 
+@pytest.mark.parametrize("w,vpt,g,wide,drain", [("8", "1", "16", "1", "1"), ("8", "2", "8", "1", "1"),
+                                                ("8", "1", "16", "0", "0"), ("3", "2", "8", "1", "0")])
+def test_all_to_all_ticket_kernel_reads_bases_from_lanes(asm, w, vpt, g, wide, drain):
+    """The all-to-all in ticket order: the table is read once before the tile loop; each tile has one
+    load and one store per vector (two batches of G tiles per unrolled trip); its destination base comes
+    from the lanes that hold the translated bases (two readlanes with a scalar lane index), never from
+    memory; no store is preceded by a full drain except after each ticket's atomic where the launch asks."""
+    sym, lines = _kernel_body(asm["ag_copy.hip"], f"ag_a2a_ticket_kernelILi{w}ELi{vpt}ELi{g}ELb{wide}ELb{drain}E")
+    G, VPT = int(g), int(vpt)
+    h, b = _outermost(_loops(lines))
+    body, prologue = lines[h:b + 1], lines[:h]
+    assert sum(ln.startswith("global_load_dwordx2") for ln in prologue) == 1      # the table, once
+    assert not any(ln.startswith("global_load") for ln in body)
+    assert all(re.match(r"s_load_dwordx2 s\[\d+:\d+\], s\[\d+:\d+\], 0x60$", ln)
+               for ln in body if ln.startswith("s_load")), [ln for ln in body if ln.startswith("s_load")]
+    assert any(ln.startswith("global_atomic_inc") for ln in lines)
+    loads = [ln for ln in body if ln.startswith("buffer_load")]
+    stores = [i for i, ln in enumerate(body) if ln.startswith("buffer_store")]
+    assert len(loads) == 2 * G * VPT and len(stores) == 2 * G * VPT
+    # (readlanes with a constant lane index are the compiler's scalar spills to vector lanes)
+    reads = [ln for ln in body if re.fullmatch(r"v_readlane_b32 s\d+, v\d+, s\d+", ln)]
+    assert len(reads) == 2 * 2 * G, len(reads)
+    drains = [i for i, ln in enumerate(body) if ln.startswith("s_waitcnt") and "vmcnt(0)" in ln]
+    if drain == "0":
+        assert not [i for i in drains if i < stores[-1]], [body[i] for i in drains]
+    else:
+        assert len(drains) == 2 and all(any(ln.startswith("global_atomic_inc") for ln in body[i - 3:i]) for i in drains)
+    assert not _sign_extended_lane_reads(lines)
+    assert _meta(asm["ag_copy.hip"], sym)["scratch"] == 0
+
+
 _SIGN_OPS = ("s_ashr_i32", "s_ashr_i64", "s_bfe_i32", "s_bfe_i64", "s_sext_i32_i8", "s_sext_i32_i16",
              "v_ashrrev_i32", "v_ashrrev_i64", "v_bfe_i32")
 

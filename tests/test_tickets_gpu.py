@@ -14,7 +14,7 @@ import torch
 
 from gemm_all_gather_amd import binding as ag
 from gemm_all_gather_amd import inputs as gen
-from oracle import all_gather_oracle
+from oracle import all_gather_oracle, all_to_all_oracle
 from tests.gpu_util import TorchHeap, log, require_gpu, to_device
 
 pytestmark = pytest.mark.gpu
@@ -120,6 +120,67 @@ def test_ticket_order_every_world_on_every_cu(W, dtype):
         _check(th, before, ins, S, start, stride, 0)
     finally:
         th.close()
+
+
+_A2A_CASES = []
+_rng2 = np.random.default_rng(37)
+for W, (start, stride), M, N in itertools.product([1, 2, 3, 5, 8], [(0, 1), (1, 2), (3, 1)], [1, 7, 64, 300],
+                                                  [256, 264, 520, 4104]):
+    if start + (W - 1) * stride >= 8:
+        continue
+    _A2A_CASES.append((W, start, stride, M, N))
+_A2A_CASES = [c for c in _A2A_CASES if _rng2.random() < 0.35]
+
+
+def _a2a_tickets(W, start, stride, M, N, dtype, tile, programs, off, seed):
+    e = E[dtype]
+    S = ((off + W * M * N * e + 300) // 256 + 1) * 256
+    th = TorchHeap(8, S)
+    try:
+        ins = [gen.random_bit_patterns((W * M, N), e, seed, j) for j in range(W)]
+        dev = [to_device(x) for x in ins]
+        p = ag.plan_all_to_all_ex(th.view(start).geometry(), W, start, stride, dev[0], off, M, N, dtype, *tile,
+                                  programs, tile_order="tickets")
+        assert p.tile_order == ag.AG_ORDER_TICKETS and p.tiles_per_ticket in (8, 16)
+        log(f"all-to-all tickets W={W} group=({start},{stride}) M_chunk={M} N={N} {dtype} tile={tile} "
+            f"programs={programs} off={off} G={p.tiles_per_ticket} wait={p.ticket_wait} grid={p.n_programs}")
+        before = th.host()
+        for j in range(W):
+            ag.all_to_all_ex(th.view(start + j * stride), W, start, stride, dev[j], off, M, N, dtype, *tile, programs,
+                             tile_order="tickets")
+        got = th.host()
+        want = all_to_all_oracle(before, S, ins, start, stride, off)
+        if not np.array_equal(got, want):
+            bad = np.flatnonzero(got != want)
+            raise AssertionError(f"{bad.size} bytes differ; first at region {bad[0] // S} offset {bad[0] % S}")
+        assert not _counters(th).any(), "a tile counter was left non-zero"
+        return p
+    finally:
+        th.close()
+
+
+@pytest.mark.parametrize("W,start,stride,M,N", _A2A_CASES)
+def test_all_to_all_ticket_order_sweep(W, start, stride, M, N):
+    """The all-to-all in ticket order: W chunk copies as one tile sequence, G tiles per ticket."""
+    require_gpu()
+    rng = np.random.default_rng([W, start, stride, M, N, 9])
+    dtype = ["f16", "bf16", "f32"][int(rng.integers(0, 3))]
+    tiles = [(8, 256), (4, 512), (16, 128), (8, 512), (16, 256)] if E[dtype] == 2 else [(8, 256), (4, 256), (2, 512)]
+    tile = tiles[int(rng.integers(0, len(tiles)))]
+    programs = [1, 3, 7, 64, 256, 10_000][int(rng.integers(0, 6))]
+    off = 16 * int(rng.integers(0, 8))
+    _a2a_tickets(W, start, stride, M, N, dtype, tile, programs, off, seed=W * 100 + M)
+
+
+@pytest.mark.parametrize("W", [2, 5, 8])
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_all_to_all_ticket_order_on_every_cu(W, dtype):
+    """A program per CU and at least 3400 tiles in the sequence: every program takes tickets, after the
+    stores of the batch before (16 tiles of 8x256 fp16 or 8 of fp32 per ticket), with ragged columns."""
+    require_gpu()
+    M, N = 8 * -(-200 // W), 4104
+    p = _a2a_tickets(W, 0 if W > 2 else 1, 1 if W > 2 else 2, M, N, dtype, (8, 256), 0, 0, seed=W + 40)
+    assert p.n_programs >= 192 and p.ticket_wait == 1
 
 
 def test_ticket_order_repeated_calls_and_counter_reset():
