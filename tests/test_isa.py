@@ -468,7 +468,7 @@ def test_fragment_hazard_check_catches_a_missing_wait():
 def test_report_registers(asm, capsys):
     """Print VGPR/AGPR/SGPR/scratch/LDS per instantiation (reported next to timings)."""
     rows = []
-    for src, pat in (("ag_copy.hip", r"ag_(copy|a2a|copy_ticket)_kernel\S+"), ("ag_gemm.hip", r"ag_gemm_kernel\S+")):
+    for src, pat in (("ag_copy.hip", r"ag_(copy|a2a|copy_ticket|a2a_ticket)_kernel\S+"), ("ag_gemm.hip", r"ag_gemm_kernel\S+")):
         for sym in re.findall(r"^\s*\.amdhsa_kernel (\S+)\s*$", asm[src], re.M):
             if re.search(pat, sym):
                 rows.append((sym, _meta(asm[src], sym)))
@@ -483,7 +483,8 @@ def test_report_registers(asm, capsys):
              r"ag_copy_kernelILi16ELi8ELi2ELi0ELb0ELb1E",
              r"ag_copy_kernelILi16ELi8ELi1ELi1ELb0ELb0E", r"ag_copy_kernelILi16ELi8ELi1ELi2ELb0ELb0E",
              r"ag_copy_kernelILi16ELi8ELi1ELi4ELb0ELb0E", r"ag_copy_kernelILi16ELi1ELi1ELi0ELb1ELb1E",
-             r"ag_a2a_kernelILi16ELi8ELi2ELb1E",
+             r"ag_a2a_kernelILi16ELi8ELi2ELb1E", r"ag_a2a_ticket_kernelILi8ELi2ELi8ELb1ELb1E",
+             r"ag_a2a_ticket_kernelILi8ELi2ELi8ELb1ELb0E",
              r"ag_gemm_kernelILb0ELi8E\S*CfgILi256ELi256E\S*ELb0EEEv", r"ag_gemm_kernelILb1ELi8E\S*CfgILi256ELi256E\S*ELb0EEEv",
              r"ag_gemm_kernelILb0ELi8E\S*CfgILi256ELi224E\S*ELb0EEEv", r"ag_gemm_kernelILb1ELi8E\S*CfgILi256ELi224E\S*ELb0EEEv",
              r"ag_gemm_kernelILb0ELi8E\S*CfgILi128ELi128E\S*ELb0EEEv", r"ag_gemm_kernelILb0ELi1E\S*CfgILi256ELi224E\S*ELb0EEEv",
