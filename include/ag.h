@@ -235,7 +235,7 @@ ag_status_t ag_heap_info(const ag_heap_t* heap, int* n_ranks, int* rank, size_t*
  *               W*M_local x N output inside every member region
  * tile_m,tile_n tile of the persistent loop; 0,0 = 8x256.  Powers of two with
  *               tile_n in [8, 4096], tile_m in [1, 256]; one tile must hold
- *               between 1 and 16 vector accesses per thread of a 256-thread
+ *               between 1 and 8 vector accesses per thread of a 256-thread
  *               workgroup at the vector width chosen (AG_ERR_UNSUPPORTED
  *               otherwise)
  * n_programs    persistent workgroups; 0 = number of CUs
@@ -350,8 +350,11 @@ ag_status_t ag_all_gather_noalloc(const ag_heap_t* heap, int W, int rank_start, 
  * in rotated order; each tile is loaded once and stored once.  Tiles as for
  * ag_all_gather (0,0 = 8x256): 1 to 8 vectors per thread of a 256-thread
  * workgroup (AG_ERR_UNSUPPORTED otherwise; 8x256 always fits); W x tiles per
- * chunk below 2^31.  M_chunk = 0 is a no-op.  input must not overlap any
- * member's output block.
+ * chunk below 2^31.  Calls for different ranks may run concurrently on
+ * different streams; calls for the same rank must not overlap in time (a
+ * call in ticket order uses the rank's counter, as ag_all_gather does).
+ * M_chunk = 0 is a no-op.  input must not overlap any member's output
+ * block.
  * ------------------------------------------------------------------------ */
 ag_status_t ag_all_to_all(const ag_heap_t* heap, int W, int rank_start, int rank_stride,
                           const void* input, size_t out_offset, int64_t M_chunk, int64_t N,
