@@ -57,7 +57,7 @@ typedef enum ag_status {
 typedef enum ag_dtype {
     AG_F16 = 0,   /* IEEE binary16, 2 bytes */
     AG_BF16 = 1,  /* bfloat16, 2 bytes */
-    AG_F32 = 2    /* IEEE binary32, 4 bytes (all-gather only) */
+    AG_F32 = 2    /* IEEE binary32, 4 bytes (the copies only, not the GEMM) */
 } ag_dtype_t;
 
 /* Largest group the kernels are instantiated for (destination loop is a static unroll). */
@@ -105,7 +105,8 @@ typedef struct ag_plan {
 
 /* Tile schedules of the all-gather (ag_all_gather_ex) and the all-to-all (ag_all_to_all_ex). */
 typedef enum ag_schedule {
-    AG_SCHEDULE_TILES = 0,       /* each program walks tiles and stores every tile to all W destinations */
+    AG_SCHEDULE_TILES = 0,       /* each program walks tiles and stores every tile to all W destinations
+                                    (the all-to-all: each chunk tile to its one destination) */
     AG_SCHEDULE_PARTITIONED = 1  /* each program owns one destination and walks the tiles for it alone */
 } ag_schedule_t;
 
@@ -190,7 +191,8 @@ ag_status_t ag_heap_reset(ag_heap_t* heap);
 /* Zero every rank's tile counters (the ticket order's; see ag_all_gather) with a small kernel on stream
  * (hipStream_t; no memset, so the call can be captured in a graph).  The counters are zero between calls
  * and need no clearing in correct use; this restores them after calls of one rank overlapped in time,
- * which the all-gather does not allow and which can leave a counter non-zero for the rank's later calls.
+ * which the all-gather and the all-to-all do not allow and which can leave a counter non-zero for the
+ * rank's later calls.
  * Stream-ordered; no call of this heap may run concurrently with it. */
 ag_status_t ag_heap_clear_tickets(const ag_heap_t* heap, void* stream);
 
