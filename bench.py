@@ -662,6 +662,9 @@ def main() -> int:
                 "alg_flops_per_launch": flops,
                 "avg_launch_us": round(fu_launch_s * 1e6, 3),
             },
+            # the minimum HBM bytes of a call (A and B read once, the W output copies written) over its time
+            "alg_bytes_per_launch": fu_plan.bytes_read + fu_plan.bytes_written,
+            "achieved_alg_GBs": round((fu_plan.bytes_read + fu_plan.bytes_written) / fu_launch_s / 1e9, 1),
             "plan": {k: fu_plan.as_dict()[k] for k in ("tile_m", "tile_n", "tile_k", "n_programs", "threads",
                                                        "total_tiles")},
             "spread": spread.get(id(fused_job)),
