@@ -212,9 +212,9 @@ class _Workload:
         self.M, self.N, self.dtype, self.W, self.start, self.stride = M, N, dtype, W, start, stride
         self.e = 4 if dtype == "f32" else 2
         self.blk = M * N * self.e
-        # every region sized for the gathered output (2 MiB multiples)
+        # every region sized for the gathered output, laid out as ag_heap_create lays out its regions
         out_bytes = W * self.blk if out_bytes is None else out_bytes
-        self.S = -(-out_bytes // (2 << 20)) * (2 << 20)
+        self.S = ag.heap_region_bytes(out_bytes)
         self.slab = torch.empty(n_regions * self.S, dtype=torch.uint8, device="cuda")
         self.slab.zero_()
         self.heap = ag.Heap.wrap(self.slab, n_regions, self.S)
@@ -409,7 +409,7 @@ def _context_fused(args, stream, timed, views, fu_off):
         if M != FU_M:
             # a heap of its own, regions sized for this workload's gathered output, as for the
             # all-gather workloads (the region stride moves the store rate)
-            S = -(-(FU_W * M * FU_N * 2) // (2 << 20)) * (2 << 20)
+            S = ag.heap_region_bytes(FU_W * M * FU_N * 2)
             own_slab = torch.zeros(FU_W * S, dtype=torch.uint8, device="cuda")
             own = ag.Heap.wrap(own_slab, FU_W, S)
             vws, off = [own.view(r) for r in range(FU_W)], 0
@@ -530,7 +530,7 @@ def main() -> int:
         fa = [_device_normal(FU_M * FU_K, FU_DTYPE, FU_K ** -0.5, 200 + j) for j in range(FU_W)]
         fb = _device_normal(FU_N * FU_K, FU_DTYPE, FU_K ** -0.5, 300)
         fblk = FU_M * FU_N * 2
-        SF = -(-(FU_W * fblk) // (2 << 20)) * (2 << 20)
+        SF = ag.heap_region_bytes(FU_W * fblk)
         fslab = torch.empty(FU_W * SF, dtype=torch.uint8, device="cuda")
         fslab.zero_()
         fheap = ag.Heap.wrap(fslab, FU_W, SF)

@@ -88,6 +88,7 @@ _c_int, _c_size, _c_i64, _c_u64, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_i
 _HEAP_PP = ctypes.POINTER(ctypes.c_void_p)
 
 _SIGNATURES = {
+    "ag_heap_region_bytes": [_c_size, ctypes.POINTER(ctypes.c_size_t)],
     "ag_heap_create": [_c_int, _c_size, _HEAP_PP],
     "ag_heap_wrap": [_vp, _c_int, _c_size, _HEAP_PP],
     "ag_heap_view": [_vp, _c_int, _HEAP_PP],
@@ -158,6 +159,13 @@ def _check(status: int, call: str) -> None:
 
 def version() -> str:
     return lib().ag_version().decode()
+
+
+def heap_region_bytes(bytes_per_rank: int) -> int:
+    """The region stride ag_heap_create uses for bytes_per_rank (the layout to give ag_heap_wrap too)."""
+    out = ctypes.c_size_t(0)
+    _check(lib().ag_heap_region_bytes(bytes_per_rank, ctypes.byref(out)), "ag_heap_region_bytes")
+    return out.value
 
 
 def _ptr(x) -> int:

@@ -62,7 +62,7 @@ typedef enum ag_dtype {
 
 /* Largest group the kernels are instantiated for (destination loop is a static unroll). */
 #define AG_MAX_WORLD 8
-/* Alignment of every region stride created by ag_heap_create. */
+/* Alignment (and unit) of every region stride created by ag_heap_create. */
 #define AG_REGION_ALIGN ((size_t)2 << 20)
 
 typedef struct ag_heap ag_heap_t;  /* opaque */
@@ -152,8 +152,21 @@ typedef struct ag_copy_options {
  * a separate device array of n_ranks uint64_t.
  * ------------------------------------------------------------------------ */
 
-/* Allocate a slab of n_ranks regions of bytes_per_rank bytes (rounded up to
- * AG_REGION_ALIGN) plus the device base table, on the current device.  The
+/* The region stride ag_heap_create uses for bytes_per_rank (ROCm/iris #594
+ * "Local validation": logical ranks as separate memory of one GPU; how the
+ * regions sit in HBM is this library's choice).  bytes_per_rank rounded up
+ * to AG_REGION_ALIGN, plus one AG_REGION_ALIGN when the result is a power of
+ * two of 512 MiB or more: the W copies of a tile are stored at the same
+ * offset of W regions at once, and strides of a large power of two alias
+ * them in the HBM channel interleave (W=8, 16384x8192 fp16 per rank: 349-354
+ * against 354-360 us per call).  Callers of ag_heap_wrap can lay out their
+ * slab the same way.  Host-only.  AG_ERR_INVALID_ARG when region_bytes is
+ * NULL or bytes_per_rank is 0 or above 1 TiB. */
+ag_status_t ag_heap_region_bytes(size_t bytes_per_rank, size_t* region_bytes);
+
+/* Allocate a slab of n_ranks regions of bytes_per_rank bytes (the region
+ * stride is ag_heap_region_bytes(bytes_per_rank)) plus the device base
+ * table, on the current device.  The
  * heap owns both.  n_ranks in [1, 1024], bytes_per_rank >= 1.  Contents of
  * the slab are undefined.  AG_ERR_OUT_OF_MEMORY if hipMalloc fails,
  * AG_ERR_HIP if no device is usable. */

@@ -235,6 +235,22 @@ def test_gemm_plan_rejects(over, status):
     assert got == status, (over, got, msg)
 
 
+@pytest.mark.parametrize("nbytes,want_mib", [(1, 2), (3 * MiB, 4), (256 * MiB, 256), (510 * MiB + 1, 512 + 2),
+                                            (512 * MiB, 514), (1024 * MiB, 1026), (2048 * MiB - 7, 2050),
+                                            (2048 * MiB + 1, 2050), (1536 * MiB, 1536), (8 * 16384 * 3584 * 2, 896)])
+def test_heap_region_bytes(nbytes, want_mib):
+    # whole 2 MiB units, one more when that is a power of two from 512 MiB (the W copies of a tile would
+    # alias in the HBM channel interleave)
+    assert ag.heap_region_bytes(nbytes) == want_mib * MiB
+
+
+def test_heap_region_bytes_rejects():
+    assert status_of(ag.heap_region_bytes, 0)[0] == ag.AG_ERR_INVALID_ARG
+    assert status_of(ag.heap_region_bytes, (1 << 40) + 1)[0] == ag.AG_ERR_INVALID_ARG
+    got = ag.lib().ag_heap_region_bytes(MiB, None)
+    assert got == ag.AG_ERR_INVALID_ARG
+
+
 def test_heap_create_without_device_reports_hip_error():
     import torch
     if torch.cuda.is_available():

@@ -182,6 +182,11 @@ def test_library_owned_heap_create_and_alloc():
     require_gpu()
     log("ag_heap_create + ag_heap_alloc path")
     R, W, M, N = 4, 4, 100, 300
+    big = ag.Heap.create(2, 512 << 20)   # a power-of-two region of 512 MiB gets one more 2 MiB unit
+    try:
+        assert big.geometry().bytes_per_rank == (512 + 2) << 20 == ag.heap_region_bytes(512 << 20)
+    finally:
+        big.destroy()
     heap = ag.Heap.create(R, 3 << 20)
     try:
         g = heap.geometry()
